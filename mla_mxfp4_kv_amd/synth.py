@@ -1,0 +1,136 @@
+"""Seeded synthetic inputs for MXFP4-KV MLA decode.
+
+This module only MAKES inputs: random bf16 queries, random latent rows and
+their MXFP4 encoding (the cache the decode reads). It holds none of the decode
+arithmetic (no dequantisation, no attention) and imports neither the HIP
+library nor the oracle, so both can be fed from it.
+
+Recipe (one generator, draws in a fixed order: lengths, Q, KV):
+
+* lengths: uniform kv_len, or integers uniform in [lo, hi] inclusive (drawn
+  from a CPU generator so the lengths do not depend on the device);
+* Q: float32 ``randn * q_std`` rounded to bf16, shape [B, 16, 576];
+* KV latent rows: float32 ``randn`` [T, 576], optionally multiplied per token
+  by ``2^u`` with u ~ U[-2, 2] (scales log-uniform in [0.25, 4]), rounded to
+  bf16, then MXFP4-encoded by :func:`quantize_mxfp4`.
+
+The rows are generated in fixed-size chunks so that a given (seed, device)
+always yields the same bytes whatever the total size.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+NUM_HEADS = 16
+QK_DIM = 576
+PACKED_BYTES = 288
+SCALES_PER_TOKEN = 18
+_ROW_CHUNK = 65536
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    kv_len: int | None          # uniform length, or None when ragged
+    ragged: tuple | None        # (lo, hi) inclusive, or None
+    q_std: float
+    token_scale: bool           # per-token multiplier 2^U[-2,2]
+    seed: int
+    sm_scale: float = 1.0 / math.sqrt(576.0)
+
+
+# The five synthetic workloads (shapes of the leaderboard's MI355X decode
+# cases plus a long single context and a ragged batch).
+WORKLOADS = {
+    "b4_kv1024": Workload("b4_kv1024", 4, 1024, None, 1.0, False, 0),
+    "b1_kv65536": Workload("b1_kv65536", 1, 65536, None, 1.0, False, 1),
+    "b64_kv8192_tokscale": Workload("b64_kv8192_tokscale", 64, 8192, None, 1.0, True, 2),
+    "b256_kv8192": Workload("b256_kv8192", 256, 8192, None, 1.0, False, 3),
+    "b128_ragged": Workload("b128_ragged", 128, None, (256, 32768), 2.0, False, 4),
+}
+
+
+def quantize_mxfp4(x: torch.Tensor):
+    """MXFP4-encode rows of 576 values (any float dtype, any device).
+
+    Per 32-element block: shared exponent ``E = floor(log2(amax)) - 2``
+    (exactly, from ``frexp``), stored as the E8M0 byte ``E + 127`` clamped to
+    [0, 254]; an all-zero block stores 127. Each element ``x / 2^E`` is rounded
+    to the nearest e2m1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the code
+    with an even mantissa bit, saturating at 6; the sign bit is set for
+    negative inputs. Codes are packed two per byte, element 2j in the low
+    nibble of byte j. Returns (packed uint8 [N, 288], scales uint8 [N, 18]).
+    """
+    if x.dim() != 2 or x.shape[1] != QK_DIM:
+        raise ValueError("x must be [N, 576]")
+    n = x.shape[0]
+    xd = x.to(torch.float64).reshape(n, SCALES_PER_TOKEN, 32)
+    amax = xd.abs().amax(dim=2)
+    _, e = torch.frexp(amax)                     # amax = m * 2^e, m in [0.5, 1)
+    byte = (e.to(torch.int32) - 3 + 127).clamp(0, 254)
+    byte = torch.where(amax > 0, byte, torch.full_like(byte, 127))
+    shift = (byte - 127).to(torch.float64)
+    y = xd * torch.exp2(-shift).unsqueeze(2)     # exact: power-of-two scaling in fp64
+    a = y.abs()
+    # Rounding thresholds between consecutive magnitude codes; at a tie the
+    # even code wins, so the comparison is strict before an odd code and
+    # inclusive before an even one.
+    code = ((a > 0.25).to(torch.uint8) + (a >= 0.75).to(torch.uint8)
+            + (a > 1.25).to(torch.uint8) + (a >= 1.75).to(torch.uint8)
+            + (a > 2.5).to(torch.uint8) + (a >= 3.5).to(torch.uint8)
+            + (a > 5.0).to(torch.uint8))
+    code = code | ((y < 0).to(torch.uint8) << 3)
+    code = code.reshape(n, QK_DIM)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, byte.to(torch.uint8).contiguous()
+
+
+def seq_lengths(w: Workload) -> list:
+    """Per-sequence KV lengths of a workload (device independent)."""
+    if w.ragged is None:
+        return [int(w.kv_len)] * w.batch
+    g = torch.Generator().manual_seed(w.seed)
+    lo, hi = w.ragged
+    return [int(v) for v in torch.randint(lo, hi + 1, (w.batch,), generator=g)]
+
+
+def make_inputs(w: Workload, device="cpu", lengths=None):
+    """Build (q bf16 [B,16,576], packed u8 [T,288], scales u8 [T,18],
+    kv_indptr int32 [B+1] on the host, lengths list) on ``device``.
+
+    ``lengths`` overrides the workload's length rule (for small test cases).
+    """
+    device = torch.device(device)
+    lens = seq_lengths(w) if lengths is None else [int(v) for v in lengths]
+    batch = len(lens)
+    indptr = [0]
+    for n in lens:
+        indptr.append(indptr[-1] + n)
+    total = indptr[-1]
+    g = torch.Generator(device=device).manual_seed(w.seed + 1000)
+    q = (torch.randn(batch, NUM_HEADS, QK_DIM, generator=g, device=device,
+                     dtype=torch.float32) * w.q_std).to(torch.bfloat16)
+    packed = torch.empty(total, PACKED_BYTES, dtype=torch.uint8, device=device)
+    scales = torch.empty(total, SCALES_PER_TOKEN, dtype=torch.uint8, device=device)
+    for r0 in range(0, total, _ROW_CHUNK):
+        r1 = min(total, r0 + _ROW_CHUNK)
+        x = torch.randn(r1 - r0, QK_DIM, generator=g, device=device, dtype=torch.float32)
+        if w.token_scale:
+            u = torch.rand(r1 - r0, 1, generator=g, device=device, dtype=torch.float32)
+            x = x * torch.exp2(4.0 * u - 2.0)
+        x = x.to(torch.bfloat16)
+        pk, sc = quantize_mxfp4(x)
+        packed[r0:r1] = pk
+        scales[r0:r1] = sc
+    kv_indptr = torch.tensor(indptr, dtype=torch.int32)
+    return q, packed, scales, kv_indptr, lens
+
+
+def kv_bytes(total_tokens: int) -> int:
+    """Algorithmic KV-cache bytes a decode call must read (packed + scales)."""
+    return total_tokens * (PACKED_BYTES + SCALES_PER_TOKEN)

@@ -1,0 +1,42 @@
+"""CPU oracle for MXFP4-KV absorbed-MLA decode.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this package:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call it. It shares no code with the HIP library
+under ``mla_mxfp4_kv_amd/`` and never imports it.
+
+Sources (kernelindex.com "amd-mixed-mla" leaderboard submission pages):
+
+* page "kernelbot-amd-mixed-mla-608791" -- HIP MXFP4 split-K submission:
+  the constants block (16 heads, 576/512 dims, 32-element scale blocks,
+  288 packed bytes per token), the ``kFp4Lut`` value table, ``e8m0_to_float``,
+  ``unpack_mxfp4`` and the stage-1 tile fill (nibble order, scale index).
+* page "kernelbot-amd-mixed-mla-717900" -- Triton MXFP4 flash-decode:
+  the layout comment block (nibble order, E8M0 = 2^(byte-127)) and
+  ``_nibble_to_f32`` (arithmetic statement of the e2m1 values).
+* page "kernelbot-amd-mixed-mla-676098" -- Triton bf16 flash-decode:
+  ``_naive_fallback`` (the plain softmax(scale*q.k) v definition with v = the
+  first 512 latent dims of the same rows).
+
+Modules:
+
+* :mod:`oracle.mxfp4_ref` -- exact MXFP4 dequantisation and fp64 attention.
+* :mod:`oracle.planner_ref` -- the CPU reference work-list planner.
+"""
+
+from .mxfp4_ref import (  # noqa: F401
+    E2M1_VALUES,
+    NUM_HEADS,
+    QK_DIM,
+    V_DIM,
+    SCALE_BLOCK,
+    PACKED_BYTES,
+    SCALES_PER_TOKEN,
+    bf16_bits_to_f64,
+    e2m1_value,
+    e8m0_scale,
+    dequant_mxfp4,
+    mla_decode_ref,
+    mla_decode_ref_seq,
+)
+from .planner_ref import plan_words_ref, PlanRef, decode_plan_words  # noqa: F401
