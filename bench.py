@@ -1,0 +1,197 @@
+"""Benchmark: MXFP4-KV absorbed-MLA decode on one MI355X.
+
+A step is one decode call (split-K decode kernel + reduce kernel when some
+sequence is split) over one batch of synthetic inputs already resident in
+HBM. Default workload: B=256 sequences x 8192 tokens (641.7 MB of packed KV +
+E8M0 scales). Prints one JSON line with the metric (KV-cache GB/s), us/call,
+the roofline of the decode kernel (HIP-event timing on the launch stream) and
+the CPU oracle timed on a bounded sample as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import torch
+
+from mla_mxfp4_kv_amd import binding, synth
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+QO_BYTES_PER_SEQ = 16 * 576 * 2 + 16 * 512 * 2
+PARTIAL_BYTES = 16 * (512 + 1) * 4
+
+
+def algorithmic_bytes(words, total_tokens):
+    """Bytes the decode must move: KV + scales, Q, output, and each split
+    partial written once and read once."""
+    num_partials = words[9]
+    batch = words[2]
+    return (synth.kv_bytes(total_tokens) + batch * QO_BYTES_PER_SEQ
+            + 2 * num_partials * PARTIAL_BYTES)
+
+
+def cpu_baseline(w, q, packed, scales, lens, budget_s):
+    """Time the fp64 oracle (as it stands) on whole sequences of the same
+    workload until about ``budget_s`` seconds of CPU work."""
+    import numpy as np
+    from oracle import mxfp4_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = torch.get_num_threads()
+    qb = q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    ind = [0]
+    for n in lens:
+        ind.append(ind[-1] + n)
+    done_tokens = 0
+    n_seq = 0
+    oracle_s = 0.0
+    for b in range(len(lens)):
+        lo, hi = ind[b], ind[b + 1]
+        pk = packed[lo:hi].cpu().numpy()
+        sc = scales[lo:hi].cpu().numpy()
+        t0 = time.perf_counter()          # device->host copies are not timed
+        mxfp4_ref.mla_decode_ref_seq(qb[b], pk, sc, w.sm_scale)
+        oracle_s += time.perf_counter() - t0
+        done_tokens += hi - lo
+        n_seq += 1
+        if oracle_s >= budget_s:
+            break
+    gbs = synth.kv_bytes(done_tokens) / oracle_s / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {n_seq} of {len(lens)} sequences ({done_tokens} tokens) of {w.name}, "
+                  f"{oracle_s:.1f} s, us/call extrapolated "
+                  f"{oracle_s / done_tokens * sum(lens) * 1e6:.0f}",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b256_kv8192", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the cpu_baseline (0 = skip)")
+    ap.add_argument("--cold", action="store_true",
+                    help="flush the L2/MALL with a 1 GB write before every timed call")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the single-GPU decode kernel; multi-GPU runs are not part "
+              "of this build (one GPU per box). Use --gpus 1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        return 2
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    q, packed, scales, indptr, lens = synth.make_inputs(w, device=dev)
+    total = int(indptr[-1])
+    t_plan = time.perf_counter()
+    dec = binding.MlaDecode(indptr.tolist(), device=dev)
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
+    words, _ = binding.plan_host(indptr.tolist(), binding.num_cus())
+    out = torch.empty(w.batch, 16, 512, dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        ev0[i].record(stream)
+        dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    call_us = [a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)]
+    avg_us = statistics.fmean(call_us)
+    med_us = statistics.median(call_us)
+    ms_per_step = wall / args.steps * 1e3
+    kvb = synth.kv_bytes(total)
+    # whole-job throughput (wall clock over the timed steps); with --cold the
+    # wall clock includes the flushes, so the event time is used instead
+    step_s = (avg_us * 1e-6) if args.cold else (wall / args.steps)
+    value = kvb / step_s / 1e9
+    alg = algorithmic_bytes(words, total)
+    achieved = alg / (avg_us * 1e-6) / 1e9
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, q, packed, scales, lens, args.cpu_budget)
+
+    line = {
+        "metric": "KV-cache HBM GB/s (us/call), MXFP4 MLA decode",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(avg_us, 2),
+        "us_per_call_median": round(med_us, 2),
+        "us_per_call_p10_p90": [round(sorted(call_us)[int(0.1 * (len(call_us) - 1))], 2),
+                                round(sorted(call_us)[int(0.9 * (len(call_us) - 1))], 2)],
+        "plan_ms": round(plan_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (MXFP4 e2m1/E8M0 KV, fp32 accumulate)",
+        "data": "synthetic",
+        "cold": bool(args.cold),
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "kv_len": w.kv_len if w.kv_len is not None else f"U{list(w.ragged)}",
+            "total_tokens": total,
+            "heads": 16,
+            "qk_dim": 576,
+            "v_dim": 512,
+            "kv_bytes": kvb,
+            "num_partials": words[9],
+            "num_slots": words[7],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": alg,
+            "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,146 @@
+/*
+ * mla_mxfp4.h -- C ABI of libmla_mxfp4.so: MXFP4-KV absorbed-MLA decode for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (kernelindex.com "amd-mixed-mla" submission pages):
+ *   For each sequence b (one query token) and head h in 0..15,
+ *     out[b,h,:] = sum_t softmax_t(sm_scale * q[b,h,:] . K[t,:]) * V[t,:]
+ *   over the tokens t of b, where K[t,:] (576 values) is the MXFP4-decoded
+ *   latent+rope row and V[t,:] = K[t,0:512]. Definition: page
+ *   "kernelbot-amd-mixed-mla-676098", _naive_fallback; shapes and the cache
+ *   layout: page "kernelbot-amd-mixed-mla-608791", constants block and
+ *   stage-1 kernel.
+ *
+ * Data layouts (all row-major and contiguous):
+ *   q         bf16  [B, 16, 576]   device, 16-byte aligned
+ *   kv_packed uint8 [T, 288]       device, 16-byte aligned. Element j of a
+ *             token is the low nibble (j even) or high nibble (j odd) of byte
+ *             j/2, an OCP e2m1 code ("kernelbot-amd-mixed-mla-608791",
+ *             kFp4Lut and the stage-1 tile fill).
+ *   kv_scale  uint8 [T, 18]        device, any alignment. E8M0 byte e scales
+ *             elements 32k..32k+31 by 2^(e-127); e = 255 is NaN
+ *             ("kernelbot-amd-mixed-mla-608791", e8m0_to_float).
+ *   kv_indptr int32 [B+1]          non-decreasing token offsets of the
+ *             sequences (page size 1, as on the 608791 page).
+ *   out       bf16  [B, 16, 512]   device, 16-byte aligned; written, never
+ *             read. A sequence with no tokens gets zeros.
+ * The decode is exact for E8M0 bytes 2..252 (every decoded element is then a
+ * normal bf16 value); bytes 253/254 can overflow bf16 and give inf/NaN.
+ *
+ * Ownership: the caller allocates every buffer (q, cache, out, workspace) and
+ * the library allocates no device memory. mla_decode_mxfp4 never blocks the
+ * host and only enqueues kernels on the given stream, so it may be recorded
+ * in a HIP graph. All pointers stay owned by the caller.
+ *
+ * Errors: every call returns an int status (MLA_OK = 0 or a negative code);
+ * mla_last_error() gives a message for the calling thread's last failure.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
+ */
+#ifndef MLA_MXFP4_H
+#define MLA_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem constants ("kernelbot-amd-mixed-mla-608791", constants block). */
+#define MLA_NUM_HEADS 16
+#define MLA_QK_DIM 576
+#define MLA_V_DIM 512
+#define MLA_SCALE_BLOCK 32
+#define MLA_PACKED_BYTES 288
+#define MLA_SCALES_PER_TOKEN 18
+
+/* Planner constants: workgroups per compute unit, slot rounding, minimum
+ * slot length in tokens. The plan rule is stated at mla_plan below. */
+#define MLA_PLAN_WG_PER_CU 1
+#define MLA_PLAN_CHUNK_ALIGN 128
+#define MLA_PLAN_MIN_CHUNK 256
+#define MLA_PLAN_MAGIC 0x4D4C4134
+#define MLA_PLAN_VERSION 1
+#define MLA_PLAN_HEADER_WORDS 16
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID -1      /* bad argument: null/misaligned pointer, bad indptr, batch < 0, non-finite sm_scale, ... */
+#define MLA_ERR_WORKSPACE -2    /* workspace smaller than the plan needs */
+#define MLA_ERR_HIP -3          /* a HIP runtime call or kernel launch failed */
+#define MLA_ERR_DEVICE -4       /* the current device is not gfx950 */
+#define MLA_ERR_NOT_PLANNED -5  /* workspace was never passed to mla_plan */
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* mla_last_error(void);
+
+/* Number of compute units of the current HIP device (queried once per
+ * device). Returns MLA_ERR_DEVICE if the device is not gfx950. */
+int mla_device_num_cus(int32_t* num_cus);
+
+/* Upper bound, in bytes, on the workspace a plan for `batch` sequences with
+ * `total_kv` tokens needs on a device with `num_cus` compute units
+ * (num_cus <= 0: query the current device). The workspace holds the plan
+ * words followed by the split-K partials (float32 LSE [P,16] and normalised
+ * float32 outputs [P,16,512]). */
+int mla_workspace_bytes(int32_t batch, int64_t total_kv, int32_t num_cus, size_t* bytes);
+
+/* Build the work list for a host copy of kv_indptr ([batch+1]) and copy it
+ * into `workspace` (device memory, 256-byte aligned, `workspace_bytes` long)
+ * on `stream`; returns after the copy has completed. The plan stays valid
+ * for decode calls on the same kv_indptr values.
+ *
+ * Plan rule (the pages leave the split policy open; page
+ * "kernelbot-amd-mixed-mla-608791", host metadata builder, gives the role of
+ * the work list and per-batch partial index): with T = kv_indptr[B] -
+ * kv_indptr[0] tokens and G = num_cus * MLA_PLAN_WG_PER_CU workgroups,
+ * chunk = max(MLA_PLAN_MIN_CHUNK, round_up(ceil(T/G), MLA_PLAN_CHUNK_ALIGN)),
+ * and slot s owns the contiguous tokens [s*chunk, (s+1)*chunk) of the
+ * concatenated cache. Each slot is cut at sequence boundaries into items;
+ * an item covering a whole sequence writes its output directly, any other
+ * item writes a partial (acc, LSE) merged afterwards by the reduce kernel.
+ *
+ * Errors: MLA_ERR_INVALID for batch < 0, a null indptr (batch > 0),
+ * indptr[0] < 0, decreasing offsets, more than 2^31-1 tokens or a null or
+ * misaligned workspace; MLA_ERR_WORKSPACE if workspace_bytes is too small. */
+int mla_plan(const int32_t* kv_indptr_host, int32_t batch,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_plan with an explicit compute-unit count (num_cus <= 0: query the
+ * device). Used to test that results do not depend on the split. */
+int mla_plan_cus(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only planner: write the plan words for `num_cus` compute units into
+ * `words` (host, `capacity_words` int32 entries). On success *num_words is
+ * the word count and *workspace_bytes the workspace size the plan needs.
+ * Touches no GPU. MLA_ERR_WORKSPACE if capacity_words is too small (then
+ * *num_words still reports the needed count). */
+int mla_plan_host(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
+                  int32_t* words, size_t capacity_words, size_t* num_words,
+                  size_t* workspace_bytes);
+
+/* Run the decode planned into `workspace` by mla_plan (same kv_indptr
+ * values). Enqueues the split-K decode kernel and, when some sequence is
+ * split or empty, the LSE-weighted reduce kernel on `stream`; never
+ * synchronises. kv_indptr is the device copy of the offsets the plan was
+ * built from; the kernels use it to bound every item to its sequence.
+ * sm_scale is the softmax scale (1/sqrt(576) for this model).
+ *
+ * Errors (nothing is enqueued): MLA_ERR_NOT_PLANNED, MLA_ERR_INVALID (null
+ * or misaligned pointer, non-finite sm_scale), MLA_ERR_DEVICE, MLA_ERR_HIP
+ * (launch failure). Faults inside the kernels surface as HIP errors on the
+ * stream. */
+int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
+                     const int32_t* kv_indptr, void* out, float sm_scale,
+                     void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_MXFP4_H */

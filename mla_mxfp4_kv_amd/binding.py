@@ -1,0 +1,178 @@
+"""ctypes binding of libmla_mxfp4.so (argument marshalling only).
+
+Every function here forwards plain pointers and sizes to the C ABI declared in
+``include/mla_mxfp4.h``; all computation happens in the library's HIP
+kernels. PyTorch is used only for device memory and the current stream. If the
+library is missing this module raises on first use -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_mxfp4.so")
+
+MLA_OK = 0
+NUM_HEADS = 16
+QK_DIM = 576
+V_DIM = 512
+PACKED_BYTES = 288
+SCALES_PER_TOKEN = 18
+
+# Every symbol the header declares (checked by the CPU test suite).
+EXPORTS = (
+    "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
+    "mla_plan", "mla_plan_cus", "mla_plan_host", "mla_decode_mxfp4",
+)
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed with {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load the shared library once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_mxfp4_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i32p = ctypes.POINTER(ctypes.c_int32)
+    c_sizep = ctypes.POINTER(ctypes.c_size_t)
+    L.mla_status_string.argtypes = [ctypes.c_int]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_last_error.argtypes = []
+    L.mla_last_error.restype = ctypes.c_char_p
+    L.mla_device_num_cus.argtypes = [c_i32p]
+    L.mla_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, c_sizep]
+    L.mla_plan.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.mla_plan_cus.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                               ctypes.c_size_t, ctypes.c_void_p]
+    L.mla_plan_host.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_int32, c_i32p, ctypes.c_size_t,
+                                c_sizep, c_sizep]
+    L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
+                 "mla_plan_host", "mla_decode_mxfp4"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, fn: str):
+    if status != MLA_OK:
+        msg = lib().mla_last_error().decode(errors="replace")
+        raise MlaError(status, fn, msg)
+
+
+def _indptr_array(kv_indptr):
+    vals = [int(v) for v in kv_indptr]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals) - 1
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def num_cus() -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().mla_device_num_cus(ctypes.byref(n)), "mla_device_num_cus")
+    return n.value
+
+
+def workspace_bytes(batch: int, total_kv: int, num_cus: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().mla_workspace_bytes(batch, total_kv, num_cus, ctypes.byref(out)),
+           "mla_workspace_bytes")
+    return out.value
+
+
+def plan_host(kv_indptr, num_cus: int):
+    """Host planner words for ``kv_indptr`` (list of B+1 ints) -> (words, bytes)."""
+    arr, batch = _indptr_array(kv_indptr)
+    n = ctypes.c_size_t(0)
+    need = ctypes.c_size_t(0)
+    st = lib().mla_plan_host(arr, batch, num_cus, None, 0, ctypes.byref(n), ctypes.byref(need))
+    if st not in (MLA_OK, -2):
+        _check(st, "mla_plan_host")
+    words = (ctypes.c_int32 * max(1, n.value))()
+    _check(lib().mla_plan_host(arr, batch, num_cus, words, n.value, ctypes.byref(n),
+                               ctypes.byref(need)), "mla_plan_host")
+    return list(words[: n.value]), need.value
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def plan(kv_indptr_host, workspace, num_cus: int = 0, stream=None):
+    """Build the work list for ``kv_indptr_host`` into the device tensor
+    ``workspace`` (uint8, 256-byte aligned)."""
+    arr, batch = _indptr_array(kv_indptr_host)
+    _check(lib().mla_plan_cus(arr, batch, num_cus, ctypes.c_void_p(workspace.data_ptr()),
+                              workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "mla_plan")
+
+
+def decode(q, kv_packed, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
+    """Enqueue the decode of a planned workspace on ``stream`` (no sync)."""
+    _check(lib().mla_decode_mxfp4(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_packed.data_ptr()),
+        ctypes.c_void_p(kv_scale.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale),
+        ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_mxfp4")
+
+
+class MlaDecode:
+    """Holds a planned workspace for one kv_indptr and runs decode calls.
+
+    Tensors: q bf16 [B,16,576], kv_packed uint8 [T,288], kv_scale uint8
+    [T,18], all on the same HIP device; ``kv_indptr`` is a host list/tensor.
+    """
+
+    def __init__(self, kv_indptr, device="cuda", num_cus: int = 0):
+        import torch
+        ind = [int(v) for v in kv_indptr]
+        self.batch = len(ind) - 1
+        self.indptr_host = ind
+        self.device = torch.device(device)
+        self.kv_indptr = torch.tensor(ind, dtype=torch.int32, device=self.device)
+        total = ind[-1] - ind[0] if ind else 0
+        nbytes = workspace_bytes(self.batch, total, num_cus)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        assert self.workspace.data_ptr() % 256 == 0
+        plan(ind, self.workspace, num_cus=num_cus)
+
+    def __call__(self, q, kv_packed, kv_scale, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(self.batch, NUM_HEADS, V_DIM, dtype=torch.bfloat16, device=self.device)
+        _validate(q, kv_packed, kv_scale, out, self.batch)
+        if kv_packed.shape[0] < self.indptr_host[-1]:
+            raise ValueError("kv_indptr reaches past the end of the cache rows")
+        decode(q, kv_packed, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+
+def _validate(q, kv_packed, kv_scale, out, batch):
+    import torch
+    if q.dtype != torch.bfloat16 or tuple(q.shape) != (batch, NUM_HEADS, QK_DIM) or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous bf16 [{batch},16,576], got {q.dtype} {tuple(q.shape)}")
+    if kv_packed.dtype != torch.uint8 or kv_packed.dim() != 2 or kv_packed.shape[1] != PACKED_BYTES \
+            or not kv_packed.is_contiguous():
+        raise ValueError("kv_packed must be contiguous uint8 [T,288]")
+    if kv_scale.dtype != torch.uint8 or tuple(kv_scale.shape) != (kv_packed.shape[0], SCALES_PER_TOKEN) \
+            or not kv_scale.is_contiguous():
+        raise ValueError("kv_scale must be contiguous uint8 [T,18]")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (batch, NUM_HEADS, V_DIM) or not out.is_contiguous():
+        raise ValueError("out must be contiguous bf16 [B,16,512]")

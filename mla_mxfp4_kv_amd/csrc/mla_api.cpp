@@ -1,0 +1,216 @@
+// C ABI of libmla_mxfp4.so: argument validation, device checks, the plan
+// registry and kernel launches. Errors are returned as status codes with a
+// thread-local message, the C counterpart of the input checks on page
+// "kernelbot-amd-mixed-mla-608791" (check_mla_inputs / check_hip_error).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MLA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+struct DeviceInfo {
+  bool queried = false;
+  bool is_gfx950 = false;
+  int num_cus = 0;
+  size_t lds_per_block = 0;
+};
+
+std::mutex g_mu;
+std::unordered_map<int, DeviceInfo> g_devices;
+
+// What a decode call needs to launch without reading the device-side plan.
+struct PlanEntry {
+  int device;
+  int32_t num_slots;
+  int32_t num_reduce;
+  int32_t off_lse;
+  int32_t off_out;
+  size_t workspace_bytes;
+};
+std::unordered_map<uintptr_t, PlanEntry> g_plans;
+
+int current_device(int* dev, DeviceInfo* info) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_devices[*dev];
+  if (!d.queried) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, *dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.is_gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.lds_per_block = prop.sharedMemPerBlock;
+    d.queried = true;
+  }
+  *info = d;
+  if (!d.is_gfx950) return fail(MLA_ERR_DEVICE, "the current HIP device is not gfx950 (MI355X)");
+  if (d.lds_per_block < mla::decode_lds_bytes())
+    return fail(MLA_ERR_DEVICE, "device LDS per workgroup is smaller than the decode kernel needs");
+  return MLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID: return "MLA_ERR_INVALID";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE";
+    case MLA_ERR_NOT_PLANNED: return "MLA_ERR_NOT_PLANNED";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+int mla_device_num_cus(int32_t* num_cus) {
+  if (num_cus == nullptr) return fail(MLA_ERR_INVALID, "num_cus is null");
+  int dev;
+  DeviceInfo info;
+  const int st = current_device(&dev, &info);
+  if (st != MLA_OK) return st;
+  *num_cus = info.num_cus;
+  return MLA_OK;
+}
+
+int mla_workspace_bytes(int32_t batch, int64_t total_kv, int32_t num_cus, size_t* bytes) {
+  if (bytes == nullptr) return fail(MLA_ERR_INVALID, "bytes is null");
+  if (batch < 0) return fail(MLA_ERR_INVALID, "batch must be >= 0");
+  if (total_kv < 0 || total_kv > INT32_MAX) return fail(MLA_ERR_INVALID, "total_kv must be in [0, 2^31)");
+  if (num_cus <= 0) {
+    const int st = mla_device_num_cus(&num_cus);
+    if (st != MLA_OK) return st;
+  }
+  *bytes = mla::workspace_bound(batch, total_kv, num_cus);
+  return MLA_OK;
+}
+
+int mla_plan_host(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, int32_t* words,
+                  size_t capacity_words, size_t* num_words, size_t* workspace_bytes) {
+  if (num_words == nullptr || workspace_bytes == nullptr)
+    return fail(MLA_ERR_INVALID, "num_words / workspace_bytes is null");
+  mla::PlanResult p;
+  std::string err;
+  const int st = mla::build_plan(kv_indptr_host, batch, num_cus, &p, &err);
+  if (st != MLA_OK) return fail(st, err);
+  *num_words = p.words.size();
+  *workspace_bytes = p.workspace_bytes;
+  if (capacity_words < p.words.size() || (words == nullptr && !p.words.empty()))
+    return fail(MLA_ERR_WORKSPACE, "word buffer too small for the plan");
+  if (!p.words.empty()) std::memcpy(words, p.words.data(), p.words.size() * sizeof(int32_t));
+  return MLA_OK;
+}
+
+int mla_plan_cus(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int dev;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != MLA_OK) return st;
+  if (num_cus <= 0) num_cus = info.num_cus;
+  if (workspace == nullptr || !aligned(workspace, mla::kAlignBytes))
+    return fail(MLA_ERR_INVALID, "workspace must be a non-null 256-byte aligned device pointer");
+  mla::PlanResult p;
+  std::string err;
+  st = mla::build_plan(kv_indptr_host, batch, num_cus, &p, &err);
+  if (st != MLA_OK) return fail(st, err);
+  if (p.workspace_bytes > workspace_bytes) {
+    char buf[160];
+    std::snprintf(buf, sizeof(buf), "workspace too small: plan needs %zu bytes, got %zu",
+                  p.workspace_bytes, workspace_bytes);
+    return fail(MLA_ERR_WORKSPACE, buf);
+  }
+  hipError_t e = hipMemcpyAsync(workspace, p.words.data(), p.words.size() * sizeof(int32_t),
+                                hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan)");
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_plans[(uintptr_t)workspace] = PlanEntry{dev, p.num_slots, p.num_reduce, p.off_lse, p.off_out,
+                                              p.workspace_bytes};
+  }
+  return MLA_OK;
+}
+
+int mla_plan(const int32_t* kv_indptr_host, int32_t batch, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return mla_plan_cus(kv_indptr_host, batch, 0, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
+                     const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
+                     void* stream) {
+  int dev;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != MLA_OK) return st;
+  PlanEntry pe;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_plans.find((uintptr_t)workspace);
+    if (it == g_plans.end())
+      return fail(MLA_ERR_NOT_PLANNED, "workspace was not prepared by mla_plan");
+    pe = it->second;
+  }
+  if (pe.device != dev) return fail(MLA_ERR_INVALID, "workspace was planned on another device");
+  if (!std::isfinite(sm_scale)) return fail(MLA_ERR_INVALID, "sm_scale must be finite");
+  const bool any_work = pe.num_slots > 0 || pe.num_reduce > 0;
+  if (any_work) {
+    if (out == nullptr || !aligned(out, 16)) return fail(MLA_ERR_INVALID, "out must be non-null and 16-byte aligned");
+    if (kv_indptr == nullptr || !aligned(kv_indptr, 4)) return fail(MLA_ERR_INVALID, "kv_indptr must be non-null and 4-byte aligned");
+  }
+  if (pe.num_slots > 0) {
+    if (q == nullptr || !aligned(q, 16)) return fail(MLA_ERR_INVALID, "q must be non-null and 16-byte aligned");
+    if (kv_packed == nullptr || !aligned(kv_packed, 16))
+      return fail(MLA_ERR_INVALID, "kv_packed must be non-null and 16-byte aligned");
+    if (kv_scale == nullptr || !aligned(kv_scale, 2))
+      return fail(MLA_ERR_INVALID, "kv_scale must be non-null and 2-byte aligned");
+  }
+  mla::DecodeArgs a;
+  a.q = q;
+  a.kv_packed = (const uint8_t*)kv_packed;
+  a.kv_scale = (const uint8_t*)kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.out = out;
+  a.plan = (const int32_t*)workspace;
+  a.part_lse = (float*)((uint8_t*)workspace + pe.off_lse);
+  a.part_out = (float*)((uint8_t*)workspace + pe.off_out);
+  a.score_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.num_slots = pe.num_slots;
+  a.num_reduce = pe.num_reduce;
+  const int gmax = info.num_cus * MLA_PLAN_WG_PER_CU;
+  a.grid = pe.num_slots < gmax ? pe.num_slots : gmax;
+  hipError_t e = (hipError_t)mla::launch_decode(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_kernel launch");
+  e = (hipError_t)mla::launch_reduce(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_reduce_kernel launch");
+  return MLA_OK;
+}
+
+}  // extern "C"

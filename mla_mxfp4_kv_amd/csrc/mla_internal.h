@@ -1,0 +1,76 @@
+// Internal declarations shared by the host API, the planner and the kernels
+// of libmla_mxfp4.so. Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mla_mxfp4.h"
+
+namespace mla {
+
+// Plan header word indices (int32 words at the start of the workspace).
+enum PlanWord : int {
+  kPwMagic = 0,
+  kPwVersion = 1,
+  kPwBatch = 2,
+  kPwBase = 3,
+  kPwTotal = 4,
+  kPwNumCus = 5,
+  kPwChunk = 6,
+  kPwNumSlots = 7,
+  kPwNumItems = 8,
+  kPwNumPartials = 9,
+  kPwNumReduce = 10,
+  kPwOffSlot = 11,      // word offset of slot_indptr[num_slots + 1]
+  kPwOffItems = 12,     // word offset of items[num_items][4] = {b, kv_begin, kv_end, dest}
+  kPwOffReduce = 13,    // word offset of reduce[num_reduce][4] = {b, first, count, 0}
+  kPwOffLse = 14,       // byte offset of partial LSE   float [P][16]
+  kPwOffOut = 15,       // byte offset of partial output float [P][16][512]
+};
+
+constexpr int kAlignBytes = 256;
+
+struct PlanResult {
+  std::vector<int32_t> words;
+  size_t workspace_bytes = 0;
+  int32_t num_slots = 0;
+  int32_t num_reduce = 0;
+  int32_t num_partials = 0;
+  int32_t off_lse = 0;
+  int32_t off_out = 0;
+};
+
+// Host planner (mla_plan.cpp). Returns MLA_OK or MLA_ERR_INVALID with *err set.
+int build_plan(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
+               PlanResult* out, std::string* err);
+
+// Upper bound on the workspace for any indptr of this size (mla_plan.cpp).
+size_t workspace_bound(int32_t batch, int64_t total, int32_t num_cus);
+
+// Kernel launchers (mla_kernels.hip). Return the hipError_t of the launch as int.
+struct DecodeArgs {
+  const void* q;
+  const uint8_t* kv_packed;
+  const uint8_t* kv_scale;
+  const int32_t* kv_indptr;
+  void* out;
+  const int32_t* plan;    // device plan words (workspace start)
+  float* part_lse;
+  float* part_out;
+  float score_scale_log2;  // sm_scale * log2(e)
+  int32_t num_slots;
+  int32_t num_reduce;
+  int32_t grid;            // decode workgroups to launch
+};
+
+int launch_decode(const DecodeArgs& a, void* stream);
+int launch_reduce(const DecodeArgs& a, void* stream);
+
+// Dynamic LDS bytes the decode kernel needs (for validation against the device).
+size_t decode_lds_bytes();
+
+}  // namespace mla

@@ -1,0 +1,463 @@
+// HIP kernels for MXFP4-KV absorbed-MLA decode on gfx950 (MI355X).
+//
+// What is computed (kernelindex.com "amd-mixed-mla" pages): for one query
+// token per sequence and 16 heads, softmax(sm_scale * q . K) V over the
+// sequence's tokens, where K is the 576-wide MXFP4-decoded latent+rope row
+// and V its first 512 dims ("kernelbot-amd-mixed-mla-676098",
+// _naive_fallback). The split-K structure -- partial (acc, LSE) per KV range,
+// then an LSE-weighted merge -- is the one of the 608791 page (stage-1 and
+// reduce kernels) and of the 676098 page (partial and reduce kernels).
+//
+// Design for CDNA4 (one wave64 per SIMD, 4 waves per workgroup, one
+// workgroup per CU, persistent over the planner's slots):
+//  * Each wave streams its own 32-token tiles of the workgroup's KV range
+//    (tiles interleaved across the 4 waves). Packed rows (288 B) and E8M0
+//    scales (18 B) are fetched with coalesced 16-byte / 2-byte global loads
+//    one tile ahead into registers, then stored to the wave's LDS buffer:
+//    rows padded to 304 B (bank-conflict-free for all reads below) and
+//    scales transposed to [block][token] bytes.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K rows (lane = token,
+//    decoded in registers by v_cvt_scalef32_pk_bf16_fp4, which is exactly
+//    e2m1 * 2^(e-127)), B = Q^T (16 heads, held in registers for the item).
+//    The 16 heads are the MFMA's N dimension, so every K tile is used by
+//    all heads at once.
+//  * Online softmax in base 2 with a lazily updated running max (rescale
+//    only when a tile max exceeds it by more than 8), cross-lane reductions
+//    over the 4 lane groups.
+//  * O += P V on the same MFMA: V comes from the packed LDS tile through
+//    ds_read_b64_tr_b8 (8 tokens x 1 byte per lane), is decoded with each
+//    token's scale and byte-permuted into token pairs. The even and odd
+//    latent dims of a 32-dim scale block form two output tiles.
+//  * The 4 waves' (m, l, O) are merged through LDS; a whole-sequence item
+//    writes bf16 output directly, any other item writes a normalised fp32
+//    partial and its base-2 LSE for the reduce kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr int kHeads = MLA_NUM_HEADS;
+constexpr int kQkDim = MLA_QK_DIM;
+constexpr int kVDim = MLA_V_DIM;
+constexpr int kRowBytes = MLA_PACKED_BYTES;     // 288
+constexpr int kBlocks = MLA_SCALES_PER_TOKEN;   // 18
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;                       // tokens per wave step
+constexpr int kTileStride = kWaves * kTile;     // a wave's step through the range
+constexpr int kLdsRow = 304;                    // padded packed row (76 dwords)
+constexpr int kLdsRows = kTile * kLdsRow;
+constexpr int kLdsScale = kLdsRows;             // [18 blocks][32 token positions]
+constexpr int kLdsBuf = kLdsRows + kBlocks * kTile;
+constexpr int kLdsWave = 2 * kLdsBuf;           // double buffer per wave
+constexpr int kMergeFrag = kWaves * 32 * 64 * 16;
+constexpr int kMergeBytes = kMergeFrag + kWaves * 2 * kHeads * 4;
+constexpr int kLdsTotal = (kWaves * kLdsWave > kMergeBytes) ? kWaves * kLdsWave : kMergeBytes;
+constexpr float kTau = 8.0f;                    // lazy-rescale threshold (base-2 units)
+constexpr float kNegInf = -__builtin_inff();
+
+static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
+
+// Register staging of one 32-token tile: 576 x 16-byte chunks of packed rows
+// (9 per lane) and 288 x 2-byte scale pairs (5 per lane, the last one only
+// for lanes < 32).
+struct Stage {
+  u32x4_t kv[9];
+  uint32_t sc[5];
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, const uint8_t* __restrict__ kv,
+                                           const uint8_t* __restrict__ sc, int t0, int ke,
+                                           int lane) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int q = 64 * i + lane;
+    const int row = q / 18;
+    const int tok = min(t0 + row, ke - 1);
+    st.kv[i] = *(const u32x4_t*)(kv + (size_t)tok * kRowBytes + 16 * (q - 18 * row));
+  }
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int u = 64 * i + lane;
+    const int row = u / 9;
+    const int tok = min(t0 + min(row, kTile - 1), ke - 1);
+    st.sc[i] = *(const uint16_t*)(sc + (size_t)tok * kBlocks + 2 * (u - 9 * row));
+  }
+}
+
+// Position of tile row (token) 16*s + 4*g + r inside a transposed scale row:
+// lane group g finds its 8 tokens (both sub-tiles) in 8 consecutive bytes.
+__device__ __forceinline__ int scale_pos(int row) {
+  return 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
+}
+
+__device__ __forceinline__ void stage_store(const Stage& st, uint8_t* buf, int t0, int ke,
+                                            int lane) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int q = 64 * i + lane;
+    const int row = q / 18;
+    const bool valid = t0 + row < ke;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    *(u32x4_t*)(buf + row * kLdsRow + 16 * (q - 18 * row)) = valid ? st.kv[i] : zero;
+  }
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int u = 64 * i + lane;
+    if (u < kTile * 9) {
+      const int row = u / 9;
+      const int blk = 2 * (u - 9 * row);
+      const bool valid = t0 + row < ke;
+      // rows past the range get scale 1.0 (byte 127) and zero codes: V = 0
+      const uint32_t v = valid ? st.sc[i] : 0x7F7Fu;
+      const int pos = scale_pos(row);
+      buf[kLdsScale + blk * kTile + pos] = (uint8_t)(v & 0xFF);
+      buf[kLdsScale + (blk + 1) * kTile + pos] = (uint8_t)(v >> 8);
+    }
+  }
+}
+
+// 8 e2m1 codes (one dword, low nibble first) times 2^(e-127) -> 8 bf16.
+// The converter reads only the exponent field of the scale operand.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ float exp_field(uint32_t e8m0) {
+  return __builtin_bit_cast(float, e8m0 << 23);
+}
+
+__device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+struct WaveState {
+  f32x4_t o[32];     // O fragments: o[2B + parity] covers dims 32B + 2*col + parity
+  float m;           // running max (base-2 scaled scores) of head `col`
+  float l;           // this lane's share of the softmax denominator
+};
+
+// One 32-token tile of one wave. `buf` holds the staged tile; tokens
+// t0 .. t0+31 (those >= ke are masked).
+__device__ __forceinline__ void process_tile(const uint8_t* buf, int t0, int ke,
+                                             const bf16x8_t (&qf)[18], WaveState& ws,
+                                             float csc, int lane) {
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // ---- S^T = K Q^T for the two 16-token sub-tiles ----
+  f32x4_t s_acc[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int row = 16 * sub + col;
+    const uint8_t* rp = buf + row * kLdsRow;
+    u32x4_t c[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c[m] = *(const u32x4_t*)(rp + 16 * (4 * m + grp));
+    const u32x2_t rope = *(const u32x2_t*)(rp + 256 + 8 * grp);
+    const int pos = scale_pos(row);
+    uint32_t e[5];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) e[m] = buf[kLdsScale + (4 * m + grp) * kTile + pos];
+    e[4] = buf[kLdsScale + (16 + (grp >> 1)) * kTile + pos];
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float sc = exp_field(e[m]);
+      a0 = mfma(dequant8(c[m][0], sc), qf[4 * m + 0], a0);
+      a1 = mfma(dequant8(c[m][1], sc), qf[4 * m + 1], a1);
+      a0 = mfma(dequant8(c[m][2], sc), qf[4 * m + 2], a0);
+      a1 = mfma(dequant8(c[m][3], sc), qf[4 * m + 3], a1);
+    }
+    const float sr = exp_field(e[4]);
+    a0 = mfma(dequant8(rope[0], sr), qf[16], a0);
+    a1 = mfma(dequant8(rope[1], sr), qf[17], a1);
+    s_acc[sub] = a0 + a1;
+  }
+
+  // ---- online softmax (base 2); lane holds head `col`, tokens 4*grp+r ----
+  float x[8];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = t0 + 16 * sub + 4 * grp + r;
+      x[4 * sub + r] = tok < ke ? s_acc[sub][r] * csc : kNegInf;
+    }
+  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool need = mx > ws.m + kTau;
+  if (__ballot(need)) {
+    const float m_new = need ? mx : ws.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;
+    ws.l *= alpha;
+    ws.m = m_new;
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+    for (int n = 0; n < 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ws.o[n][r] *= al[r];
+  }
+  const float base = ws.m == kNegInf ? 0.0f : ws.m;
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(x[i] - base);
+    psum += p[i];
+  }
+  ws.l += psum;
+  const bf16x8_t pa = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+
+  // ---- O += P V: V from the packed tile via 8-bit transposing reads ----
+  // lane (col, grp) supplies row k = col/2 of its group's 8 tokens, bytes
+  // 8*(col&1).. of a 16-byte column block; it receives byte (16B + col) of
+  // all 8 tokens, in the same token order as p[0..7].
+  const int k = col >> 1;
+  const int trow = (k < 4) ? (4 * grp + k) : (16 + 4 * grp + (k - 4));
+  const uint8_t* trp = buf + trow * kLdsRow + 8 * (col & 1);
+  const uint8_t* sbp = buf + kLdsScale + 8 * grp;
+#pragma unroll
+  for (int blk = 0; blk < 16; ++blk) {
+    const u32x2_t s8 = *(const u32x2_t*)(sbp + blk * kTile);
+    const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2_t*)(trp + 16 * blk));
+    const uint32_t v0 = (uint32_t)v[0], v1 = (uint32_t)v[1];
+    // scale of token k sits in byte k%4 of s8[k/4]; move it to bits 23..30
+    const uint32_t c0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] << 23), 0));
+    const uint32_t c1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] << 15), 1));
+    const uint32_t c2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] << 7), 2));
+    const uint32_t c3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] >> 1), 3));
+    const uint32_t c4 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] << 23), 0));
+    const uint32_t c5 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] << 15), 1));
+    const uint32_t c6 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] << 7), 2));
+    const uint32_t c7 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] >> 1), 3));
+    // c_k = (V[t_k][2j], V[t_k][2j+1]); regroup into token pairs per dim
+    const u32x4_t ev = {__builtin_amdgcn_perm(c1, c0, 0x05040100u), __builtin_amdgcn_perm(c3, c2, 0x05040100u),
+                        __builtin_amdgcn_perm(c5, c4, 0x05040100u), __builtin_amdgcn_perm(c7, c6, 0x05040100u)};
+    const u32x4_t od = {__builtin_amdgcn_perm(c1, c0, 0x07060302u), __builtin_amdgcn_perm(c3, c2, 0x07060302u),
+                        __builtin_amdgcn_perm(c5, c4, 0x07060302u), __builtin_amdgcn_perm(c7, c6, 0x07060302u)};
+    ws.o[2 * blk] = mfma(pa, __builtin_bit_cast(bf16x8_t, ev), ws.o[2 * blk]);
+    ws.o[2 * blk + 1] = mfma(pa, __builtin_bit_cast(bf16x8_t, od), ws.o[2 * blk + 1]);
+  }
+}
+
+__global__ void __launch_bounds__(kThreads, 1)
+mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                  const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
+                  uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
+                  float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  const int num_slots = plan[kPwNumSlots];
+  const int32_t* slot_indptr = plan + plan[kPwOffSlot];
+  const int32_t* items = plan + plan[kPwOffItems];
+  uint8_t* wbuf = lds + wave * kLdsWave;
+
+  for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
+    const int i_begin = slot_indptr[slot];
+    const int i_end = slot_indptr[slot + 1];
+    for (int it = i_begin; it < i_end; ++it) {
+      const int b = items[4 * it + 0];
+      const int seq_lo = kv_indptr[b];
+      const int seq_hi = kv_indptr[b + 1];
+      const int kb = max(items[4 * it + 1], seq_lo);
+      const int ke = min(items[4 * it + 2], seq_hi);
+      const int dest = items[4 * it + 3];
+
+      // Q of sequence b as the B operand of S^T = K Q^T: lane (h = col,
+      // grp) holds, for k-step s, the 8 dims this lane group contracts.
+      bf16x8_t qf[18];
+      const uint16_t* qh = q + ((size_t)b * kHeads + col) * kQkDim;
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        qf[s] = *(const bf16x8_t*)(qh + 32 * (4 * (s >> 2) + grp) + 8 * (s & 3));
+#pragma unroll
+      for (int s = 16; s < 18; ++s)
+        qf[s] = *(const bf16x8_t*)(qh + 512 + 16 * grp + 8 * (s - 16));
+
+      WaveState ws;
+#pragma unroll
+      for (int n = 0; n < 32; ++n) ws.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      ws.m = kNegInf;
+      ws.l = 0.f;
+
+      __syncthreads();  // LDS of the previous item's merge is free again
+      int t0 = kb + kTile * wave;
+      int cur = 0;
+      Stage st;
+      if (t0 < ke) {
+        stage_load(st, kv, sc, t0, ke, lane);
+        stage_store(st, wbuf, t0, ke, lane);
+      }
+      for (; t0 < ke; t0 += kTileStride) {
+        const int tn = t0 + kTileStride;
+        const bool has_next = tn < ke;
+        if (has_next) stage_load(st, kv, sc, tn, ke, lane);
+        process_tile(wbuf + cur * kLdsBuf, t0, ke, qf, ws, csc, lane);
+        if (has_next) stage_store(st, wbuf + (cur ^ 1) * kLdsBuf, tn, ke, lane);
+        cur ^= 1;
+      }
+
+      // ---- merge the 4 waves' states ----
+      ws.l += __shfl_xor(ws.l, 16);
+      ws.l += __shfl_xor(ws.l, 32);
+      __syncthreads();
+      f32x4_t* frag = (f32x4_t*)lds;
+      float* stats = (float*)(lds + kMergeFrag);
+#pragma unroll
+      for (int f = 0; f < 32; ++f) frag[(wave * 32 + f) * 64 + lane] = ws.o[f];
+      if (grp == 0) {
+        stats[(2 * wave) * kHeads + col] = ws.m;
+        stats[(2 * wave + 1) * kHeads + col] = ws.l;
+      }
+      __syncthreads();
+
+      float wgt[4][kWaves];
+      float inv[4];
+      float lse[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        float mw[kWaves], lw[kWaves];
+        float mmax = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          mw[w] = stats[(2 * w) * kHeads + h];
+          lw[w] = stats[(2 * w + 1) * kHeads + h];
+          if (lw[w] != 0.f) mmax = fmaxf(mmax, mw[w]);
+        }
+        float lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          wgt[r][w] = lw[w] != 0.f ? __builtin_amdgcn_exp2f(mw[w] - mmax) : 0.f;
+          lsum += wgt[r][w] * lw[w];
+        }
+        inv[r] = lsum != 0.f ? 1.0f / lsum : 0.f;
+        lse[r] = lsum != 0.f ? mmax + __builtin_amdgcn_logf(lsum) : kNegInf;
+      }
+      // wave w handles scale blocks 4w .. 4w+3 (both dim parities)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int blk = 4 * wave + bb;
+        f32x4_t ev = {0.f, 0.f, 0.f, 0.f}, od = ev;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const f32x4_t fe = frag[(w * 32 + 2 * blk) * 64 + lane];
+          const f32x4_t fo = frag[(w * 32 + 2 * blk + 1) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ev[r] += wgt[r][w] * fe[r];
+            od[r] += wgt[r][w] * fo[r];
+          }
+        }
+        const int d = 32 * blk + 2 * col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * grp + r;
+          const float re = ev[r] * inv[r], ro = od[r] * inv[r];
+          if (dest < 0) {
+            *(uint32_t*)(out + ((size_t)b * kHeads + h) * kVDim + d) = pack2(re, ro);
+          } else {
+            *(f32x2_t*)(part_out + ((size_t)dest * kHeads + h) * kVDim + d) = f32x2_t{re, ro};
+          }
+        }
+      }
+      if (dest >= 0 && wave == 0 && col == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part_lse[(size_t)dest * kHeads + 4 * grp + r] = lse[r];
+      }
+    }
+  }
+}
+
+// LSE-weighted merge of the partials of one sequence (or zero fill of an
+// empty one). One workgroup per reduce entry; wave w handles heads 4w..4w+3;
+// lane covers 8 consecutive output dims.
+__global__ void __launch_bounds__(kThreads)
+mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
+                  const float* __restrict__ part_out, uint16_t* __restrict__ out) {
+  const int e = blockIdx.x;
+  const int32_t* ent = plan + plan[kPwOffReduce] + 4 * e;
+  const int b = ent[0];
+  const int first = ent[1];
+  const int cnt = ent[2];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+#pragma unroll 1
+  for (int hh = 0; hh < 4; ++hh) {
+    const int h = 4 * wave + hh;
+    float mmax = kNegInf;
+    for (int i = 0; i < cnt; ++i) {
+      const float v = part_lse[(size_t)(first + i) * kHeads + h];
+      if (v != kNegInf) mmax = fmaxf(mmax, v);
+    }
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    float wsum = 0.f;
+    for (int i = 0; i < cnt; ++i) {
+      const float v = part_lse[(size_t)(first + i) * kHeads + h];
+      if (v == kNegInf) continue;
+      const float w = __builtin_amdgcn_exp2f(v - mmax);
+      wsum += w;
+      const f32x4_t* src = (const f32x4_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + 8 * lane);
+      a0 += w * src[0];
+      a1 += w * src[1];
+    }
+    const float inv = wsum != 0.f ? 1.0f / wsum : 0.f;
+    a0 *= inv;
+    a1 *= inv;
+    const u32x4_t pk = {pack2(a0[0], a0[1]), pack2(a0[2], a0[3]), pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
+    *(u32x4_t*)(out + ((size_t)b * kHeads + h) * kVDim + 8 * lane) = pk;
+  }
+}
+
+}  // namespace
+
+size_t decode_lds_bytes() { return (size_t)kLdsTotal; }
+
+int launch_decode(const DecodeArgs& a, void* stream) {
+  if (a.num_slots <= 0 || a.grid <= 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(mla_decode_kernel, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (uint16_t*)a.out,
+                     a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+  return (int)hipGetLastError();
+}
+
+int launch_reduce(const DecodeArgs& a, void* stream) {
+  if (a.num_reduce <= 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce), dim3(kThreads), 0, (hipStream_t)stream,
+                     a.plan, a.part_lse, a.part_out, (uint16_t*)a.out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mla
