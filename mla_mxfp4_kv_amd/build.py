@@ -27,6 +27,8 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around VALU work
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

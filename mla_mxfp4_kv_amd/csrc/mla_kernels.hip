@@ -12,10 +12,10 @@
 // workgroup per CU, persistent over the planner's slots):
 //  * Each wave streams its own 32-token tiles of the workgroup's KV range
 //    (tiles interleaved across the 4 waves). Packed rows (288 B) and E8M0
-//    scales (18 B) are fetched with coalesced 16-byte / 2-byte global loads
-//    one tile ahead into registers, then stored to the wave's LDS buffer:
-//    rows padded to 304 B (bank-conflict-free for all reads below) and
-//    scales transposed to [block][token] bytes.
+//    scales (18 B) go straight from HBM into the wave's LDS ring of three
+//    tile buffers with direct global->LDS loads, two tiles ahead of the one
+//    being computed: rows padded to 304 B (bank-conflict-free for all reads
+//    below), scales gathered into a [block][token] byte layout.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K rows (lane = token,
 //    decoded in registers by v_cvt_scalef32_pk_bf16_fp4, which is exactly
 //    e2m1 * 2^(e-127)), B = Q^T (16 heads, held in registers for the item).
@@ -57,11 +57,17 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                       // tokens per wave step
 constexpr int kTileStride = kWaves * kTile;     // a wave's step through the range
-constexpr int kLdsRow = 304;                    // padded packed row (76 dwords)
-constexpr int kLdsRows = kTile * kLdsRow;
-constexpr int kLdsScale = kLdsRows;             // [18 blocks][32 token positions]
-constexpr int kLdsBuf = kLdsRows + kBlocks * kTile;
-constexpr int kLdsWave = 2 * kLdsBuf;           // double buffer per wave
+constexpr int kDepth = 2;                       // tiles in flight beyond the one computed
+constexpr int kNumBuf = kDepth + 1;             // LDS tile buffers per wave
+constexpr int kLdsRow = 304;                    // packed row + one 16-byte pad (19 slots)
+constexpr int kRowDma = 10;                     // 16-byte DMA instructions per tile (640 slots >= 32*19)
+constexpr int kLdsScale = kRowDma * 64 * 16;    // scale slots after the rows
+constexpr int kScalePairs = kBlocks / 2;        // 9 pairs of scale blocks
+constexpr int kScaleSlots = kScalePairs * kTile;            // 288 four-byte slots
+constexpr int kScaleDma = (kScaleSlots + 63) / 64;          // 2-byte DMA instructions (5)
+constexpr int kDmaPerTile = kRowDma + kScaleDma;
+constexpr int kLdsBuf = kLdsScale + kScaleDma * 64 * 4;
+constexpr int kLdsWave = kNumBuf * kLdsBuf;
 constexpr int kMergeFrag = kWaves * 32 * 64 * 16;
 constexpr int kMergeBytes = kMergeFrag + kWaves * 2 * kHeads * 4;
 constexpr int kLdsTotal = (kWaves * kLdsWave > kMergeBytes) ? kWaves * kLdsWave : kMergeBytes;
@@ -70,62 +76,80 @@ constexpr float kNegInf = -__builtin_inff();
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 
-// Register staging of one 32-token tile: 576 x 16-byte chunks of packed rows
-// (9 per lane) and 288 x 2-byte scale pairs (5 per lane, the last one only
-// for lanes < 32).
-struct Stage {
-  u32x4_t kv[9];
-  uint32_t sc[5];
-};
-
-__device__ __forceinline__ void stage_load(Stage& st, const uint8_t* __restrict__ kv,
-                                           const uint8_t* __restrict__ sc, int t0, int ke,
-                                           int lane) {
-#pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int q = 64 * i + lane;
-    const int row = q / 18;
-    const int tok = min(t0 + row, ke - 1);
-    st.kv[i] = *(const u32x4_t*)(kv + (size_t)tok * kRowBytes + 16 * (q - 18 * row));
-  }
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int u = 64 * i + lane;
-    const int row = u / 9;
-    const int tok = min(t0 + min(row, kTile - 1), ke - 1);
-    st.sc[i] = *(const uint16_t*)(sc + (size_t)tok * kBlocks + 2 * (u - 9 * row));
-  }
-}
-
 // Position of tile row (token) 16*s + 4*g + r inside a transposed scale row:
 // lane group g finds its 8 tokens (both sub-tiles) in 8 consecutive bytes.
 __device__ __forceinline__ int scale_pos(int row) {
   return 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
 }
 
-__device__ __forceinline__ void stage_store(const Stage& st, uint8_t* buf, int t0, int ke,
-                                            int lane) {
+// Stage one 32-token tile (tokens t0.., those >= ke replaced by token ke-1,
+// whose contribution is later multiplied by p = 0) into an LDS buffer with
+// direct global->LDS loads. A 16-byte DMA instruction writes 64 consecutive
+// 16-byte LDS slots (lane i -> slot i); a 2-byte one writes lane i's two bytes
+// into the low half of 4-byte slot i. Every lane picks the global address
+// that belongs in its slot, so the loads also lay the tile out:
+//  * rows: 19 slots per row (18 data + 1 pad), row stride 304 bytes;
+//  * scales: slot (pair q, position pos) holds the E8M0 bytes of blocks 2q
+//    and 2q+1 of the token at `pos` (scale_pos order).
+__device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
+                                          const uint8_t* __restrict__ sc, int t0, int ke,
+                                          int lane) {
 #pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int q = 64 * i + lane;
-    const int row = q / 18;
-    const bool valid = t0 + row < ke;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    *(u32x4_t*)(buf + row * kLdsRow + 16 * (q - 18 * row)) = valid ? st.kv[i] : zero;
+  for (int i = 0; i < kRowDma; ++i) {
+    const int k = 64 * i + lane;
+    int row = k / 19;
+    int chunk = k - 19 * row;
+    row = min(row, kTile - 1);
+    chunk = min(chunk, 17);
+    const int tok = min(t0 + row, ke - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(kv + (size_t)tok * kRowBytes + 16 * chunk),
+                                     (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int u = 64 * i + lane;
-    if (u < kTile * 9) {
-      const int row = u / 9;
-      const int blk = 2 * (u - 9 * row);
-      const bool valid = t0 + row < ke;
-      // rows past the range get scale 1.0 (byte 127) and zero codes: V = 0
-      const uint32_t v = valid ? st.sc[i] : 0x7F7Fu;
-      const int pos = scale_pos(row);
-      buf[kLdsScale + blk * kTile + pos] = (uint8_t)(v & 0xFF);
-      buf[kLdsScale + (blk + 1) * kTile + pos] = (uint8_t)(v >> 8);
-    }
+  for (int i = 0; i < kScaleDma; ++i) {
+    const int slot = min(64 * i + lane, kScaleSlots - 1);
+    const int pair = slot >> 5;
+    const int pos = slot & 31;
+    const int row = 16 * ((pos >> 2) & 1) + 4 * (pos >> 3) + (pos & 3);
+    const int tok = min(t0 + row, ke - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(sc + (size_t)tok * kBlocks + 2 * pair),
+                                     (MLA_LDS void*)(buf + kLdsScale + 256 * i), 2, 0, 0);
+  }
+}
+
+// Byte address of the E8M0 scale of block `blk` for tile row position `pos`.
+__device__ __forceinline__ int scale_byte(int blk, int pos) {
+  return kLdsScale + (blk >> 1) * (kTile * 4) + 4 * pos + (blk & 1);
+}
+
+// LDS reads issued from inline assembly: the compiler does not count them,
+// so their results are only used after an explicit lgkmcnt wait that names
+// the destination registers.
+__device__ __forceinline__ u32x2_t lds_tr8(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ u32x4_t lds_b128(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const MLA_LDS uint8_t*)p;
+}
+
+// Wait until at most `tiles_after` tiles of DMA are still in flight (vector
+// memory operations complete in order). The memory clobber keeps the LDS
+// reads of the tile below this point.
+__device__ __forceinline__ void wait_tiles(int tiles_after) {
+  static_assert(2 * kDmaPerTile < 64, "vmcnt field is 6 bits");
+  if (tiles_after >= 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerTile) : "memory");
+  } else if (tiles_after == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerTile) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 
@@ -179,8 +203,8 @@ __device__ __forceinline__ void process_tile(const uint8_t* buf, int t0, int ke,
     const int pos = scale_pos(row);
     uint32_t e[5];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) e[m] = buf[kLdsScale + (4 * m + grp) * kTile + pos];
-    e[4] = buf[kLdsScale + (16 + (grp >> 1)) * kTile + pos];
+    for (int m = 0; m < 4; ++m) e[m] = buf[scale_byte(4 * m + grp, pos)];
+    e[4] = buf[scale_byte(16 + (grp >> 1), pos)];
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -241,29 +265,59 @@ __device__ __forceinline__ void process_tile(const uint8_t* buf, int t0, int ke,
   // all 8 tokens, in the same token order as p[0..7].
   const int k = col >> 1;
   const int trow = (k < 4) ? (4 * grp + k) : (16 + 4 * grp + (k - 4));
-  const uint8_t* trp = buf + trow * kLdsRow + 8 * (col & 1);
-  const uint8_t* sbp = buf + kLdsScale + 8 * grp;
+  const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1));
+  const uint32_t sca = lds_addr(buf + kLdsScale + 32 * grp);
+  // Per pair q of scale blocks: two transposing reads (blocks 2q, 2q+1) and
+  // the 8 tokens' scale slots (32 bytes). One pair is in flight while the
+  // previous one is decoded.
+  u32x2_t v_cur0 = lds_tr8(tra), v_cur1 = lds_tr8(tra + 16);
+  u32x4_t s_cur0 = lds_b128(sca), s_cur1 = lds_b128(sca + 16);
 #pragma unroll
-  for (int blk = 0; blk < 16; ++blk) {
-    const u32x2_t s8 = *(const u32x2_t*)(sbp + blk * kTile);
-    const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2_t*)(trp + 16 * blk));
-    const uint32_t v0 = (uint32_t)v[0], v1 = (uint32_t)v[1];
-    // scale of token k sits in byte k%4 of s8[k/4]; move it to bits 23..30
-    const uint32_t c0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] << 23), 0));
-    const uint32_t c1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] << 15), 1));
-    const uint32_t c2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] << 7), 2));
-    const uint32_t c3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v0, __builtin_bit_cast(float, s8[0] >> 1), 3));
-    const uint32_t c4 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] << 23), 0));
-    const uint32_t c5 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] << 15), 1));
-    const uint32_t c6 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] << 7), 2));
-    const uint32_t c7 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v1, __builtin_bit_cast(float, s8[1] >> 1), 3));
-    // c_k = (V[t_k][2j], V[t_k][2j+1]); regroup into token pairs per dim
-    const u32x4_t ev = {__builtin_amdgcn_perm(c1, c0, 0x05040100u), __builtin_amdgcn_perm(c3, c2, 0x05040100u),
-                        __builtin_amdgcn_perm(c5, c4, 0x05040100u), __builtin_amdgcn_perm(c7, c6, 0x05040100u)};
-    const u32x4_t od = {__builtin_amdgcn_perm(c1, c0, 0x07060302u), __builtin_amdgcn_perm(c3, c2, 0x07060302u),
-                        __builtin_amdgcn_perm(c5, c4, 0x07060302u), __builtin_amdgcn_perm(c7, c6, 0x07060302u)};
-    ws.o[2 * blk] = mfma(pa, __builtin_bit_cast(bf16x8_t, ev), ws.o[2 * blk]);
-    ws.o[2 * blk + 1] = mfma(pa, __builtin_bit_cast(bf16x8_t, od), ws.o[2 * blk + 1]);
+  for (int q = 0; q < 8; ++q) {
+    u32x2_t v_nx0, v_nx1;
+    u32x4_t s_nx0, s_nx1;
+    if (q < 7) {
+      v_nx0 = lds_tr8(tra + 32 * (q + 1));
+      v_nx1 = lds_tr8(tra + 32 * (q + 1) + 16);
+      s_nx0 = lds_b128(sca + kTile * 4 * (q + 1));
+      s_nx1 = lds_b128(sca + kTile * 4 * (q + 1) + 16);
+      asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(v_cur0), "+v"(v_cur1), "+v"(s_cur0), "+v"(s_cur1));
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v_cur0), "+v"(v_cur1), "+v"(s_cur0), "+v"(s_cur1));
+    }
+    const uint32_t sv[8] = {s_cur0[0], s_cur0[1], s_cur0[2], s_cur0[3],
+                            s_cur1[0], s_cur1[1], s_cur1[2], s_cur1[3]};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int blk = 2 * q + half;
+      const u32x2_t v = half ? v_cur1 : v_cur0;
+      // token k's scale is byte `half` of slot k: move it to bits 23..30
+      const int sh = half ? 15 : 23;
+      uint32_t c[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const float scl = __builtin_bit_cast(float, sv[kk] << sh);
+        const uint32_t src = kk < 4 ? v[0] : v[1];
+        bf16x2_t cv;
+        switch (kk & 3) {
+          case 0: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0); break;
+          case 1: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1); break;
+          case 2: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2); break;
+          default: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3); break;
+        }
+        c[kk] = __builtin_bit_cast(uint32_t, cv);
+      }
+      // c[k] = (V[t_k][2j], V[t_k][2j+1]); regroup into token pairs per dim
+      const u32x4_t ev = {__builtin_amdgcn_perm(c[1], c[0], 0x05040100u), __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
+                          __builtin_amdgcn_perm(c[5], c[4], 0x05040100u), __builtin_amdgcn_perm(c[7], c[6], 0x05040100u)};
+      const u32x4_t od = {__builtin_amdgcn_perm(c[1], c[0], 0x07060302u), __builtin_amdgcn_perm(c[3], c[2], 0x07060302u),
+                          __builtin_amdgcn_perm(c[5], c[4], 0x07060302u), __builtin_amdgcn_perm(c[7], c[6], 0x07060302u)};
+      ws.o[2 * blk] = mfma(pa, __builtin_bit_cast(bf16x8_t, ev), ws.o[2 * blk]);
+      ws.o[2 * blk + 1] = mfma(pa, __builtin_bit_cast(bf16x8_t, od), ws.o[2 * blk + 1]);
+    }
+    if (q < 7) {
+      v_cur0 = v_nx0; v_cur1 = v_nx1; s_cur0 = s_nx0; s_cur1 = s_nx1;
+    }
   }
 }
 
@@ -313,20 +367,17 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       ws.l = 0.f;
 
       __syncthreads();  // LDS of the previous item's merge is free again
-      int t0 = kb + kTile * wave;
-      int cur = 0;
-      Stage st;
-      if (t0 < ke) {
-        stage_load(st, kv, sc, t0, ke, lane);
-        stage_store(st, wbuf, t0, ke, lane);
-      }
-      for (; t0 < ke; t0 += kTileStride) {
-        const int tn = t0 + kTileStride;
-        const bool has_next = tn < ke;
-        if (has_next) stage_load(st, kv, sc, tn, ke, lane);
-        process_tile(wbuf + cur * kLdsBuf, t0, ke, qf, ws, csc, lane);
-        if (has_next) stage_store(st, wbuf + (cur ^ 1) * kLdsBuf, tn, ke, lane);
-        cur ^= 1;
+      const int t_first = kb + kTile * wave;
+      const int ntiles = t_first < ke ? (ke - t_first + kTileStride - 1) / kTileStride : 0;
+#pragma unroll
+      for (int j = 0; j < kDepth; ++j)
+        if (j < ntiles) stage_dma(wbuf + j * kLdsBuf, kv, sc, t_first + j * kTileStride, ke, lane);
+      for (int i = 0; i < ntiles; ++i) {
+        const int t0 = t_first + i * kTileStride;
+        if (i + kDepth < ntiles)
+          stage_dma(wbuf + ((i + kDepth) % kNumBuf) * kLdsBuf, kv, sc, t0 + kDepth * kTileStride, ke, lane);
+        wait_tiles(min(kDepth, ntiles - 1 - i));
+        process_tile(wbuf + (i % kNumBuf) * kLdsBuf, t0, ke, qf, ws, csc, lane);
       }
 
       // ---- merge the 4 waves' states ----
