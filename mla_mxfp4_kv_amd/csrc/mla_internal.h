@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mla_mxfp4.h"
+#include "mla_mxfp4.h"
 
 namespace mla {
 

@@ -8,15 +8,18 @@
 // then an LSE-weighted merge -- is the one of the 608791 page (stage-1 and
 // reduce kernels) and of the 676098 page (partial and reduce kernels).
 //
-// Design for CDNA4 (one wave64 per SIMD, 4 waves per workgroup, one
-// workgroup per CU, persistent over the planner's slots):
-//  * Each wave streams its own 32-token tiles of the workgroup's KV range
-//    (tiles interleaved across the 4 waves). Packed rows (288 B) and E8M0
-//    scales (18 B) go straight from HBM into the wave's LDS ring of three
-//    tile buffers with direct global->LDS loads, two tiles ahead of the one
+// Design for CDNA4 (8 waves per workgroup = 2 per SIMD, one workgroup per
+// CU, persistent over the planner's slots):
+//  * The workgroup's KV range is cut into 32-token tiles interleaved over 4
+//    wave pairs; the two waves of a pair (same SIMD) share each tile. Packed rows (288 B) and E8M0
+//    scales (18 B) go straight from HBM into the pair's LDS ring of three
+//    tile buffers with direct global->LDS loads, one tile ahead of the one
 //    being computed: rows padded to 304 B (bank-conflict-free for all reads
-//    below), scales gathered into a [block][token] byte layout.
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K rows (lane = token,
+//    below), scales gathered into [block pair][token] slots.
+//  * One workgroup barrier per round: in round i a wave computes QK for
+//    tile i and P V for tile i-1, so independent work interleaves.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, one 16-token half of the tile
+//    per wave (scores swapped through LDS): A = K rows (lane = token,
 //    decoded in registers by v_cvt_scalef32_pk_bf16_fp4, which is exactly
 //    e2m1 * 2^(e-127)), B = Q^T (16 heads, held in registers for the item).
 //    The 16 heads are the MFMA's N dimension, so every K tile is used by
@@ -24,11 +27,12 @@
 //  * Online softmax in base 2 with a lazily updated running max (rescale
 //    only when a tile max exceeds it by more than 8), cross-lane reductions
 //    over the 4 lane groups.
-//  * O += P V on the same MFMA: V comes from the packed LDS tile through
+//  * O += P V on the same MFMA, each wave of a pair owning 256 of the 512
+//    latent dims (so O fits in 64 registers): V comes from the packed LDS tile through
 //    ds_read_b64_tr_b8 (8 tokens x 1 byte per lane), is decoded with each
 //    token's scale and byte-permuted into token pairs. The even and odd
 //    latent dims of a 32-dim scale block form two output tiles.
-//  * The 4 waves' (m, l, O) are merged through LDS; a whole-sequence item
+//  * The 4 pairs' (m, l, O) are merged through LDS; a whole-sequence item
 //    writes bf16 output directly, any other item writes a normalised fp32
 //    partial and its base-2 LSE for the reduce kernel.
 #include <hip/hip_runtime.h>
@@ -53,24 +57,27 @@ constexpr int kQkDim = MLA_QK_DIM;
 constexpr int kVDim = MLA_V_DIM;
 constexpr int kRowBytes = MLA_PACKED_BYTES;     // 288
 constexpr int kBlocks = MLA_SCALES_PER_TOKEN;   // 18
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                       // 4 pairs x 2 halves, 2 waves per SIMD
+constexpr int kPairs = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32;                       // tokens per wave step
-constexpr int kTileStride = kWaves * kTile;     // a wave's step through the range
-constexpr int kDepth = 2;                       // tiles in flight beyond the one computed
-constexpr int kNumBuf = kDepth + 1;             // LDS tile buffers per wave
+constexpr int kTile = 32;                       // tokens per pair step
+constexpr int kTileStride = kPairs * kTile;     // a pair's step through the range
+constexpr int kNumBuf = 3;                      // LDS tile buffers per pair: P V, QK, in flight
 constexpr int kLdsRow = 304;                    // packed row + one 16-byte pad (19 slots)
 constexpr int kRowDma = 10;                     // 16-byte DMA instructions per tile (640 slots >= 32*19)
 constexpr int kLdsScale = kRowDma * 64 * 16;    // scale slots after the rows
 constexpr int kScalePairs = kBlocks / 2;        // 9 pairs of scale blocks
 constexpr int kScaleSlots = kScalePairs * kTile;            // 288 four-byte slots
 constexpr int kScaleDma = (kScaleSlots + 63) / 64;          // 2-byte DMA instructions (5)
-constexpr int kDmaPerTile = kRowDma + kScaleDma;
+constexpr int kDmaHalf0 = (kRowDma + 1) / 2 + (kScaleDma + 1) / 2;  // issued by half 0 (8)
+constexpr int kDmaHalf1 = kRowDma / 2 + kScaleDma / 2;              // issued by half 1 (7)
 constexpr int kLdsBuf = kLdsScale + kScaleDma * 64 * 4;
-constexpr int kLdsWave = kNumBuf * kLdsBuf;
-constexpr int kMergeFrag = kWaves * 32 * 64 * 16;
-constexpr int kMergeBytes = kMergeFrag + kWaves * 2 * kHeads * 4;
-constexpr int kLdsTotal = (kWaves * kLdsWave > kMergeBytes) ? kWaves * kLdsWave : kMergeBytes;
+constexpr int kLdsPair = kNumBuf * kLdsBuf;
+constexpr int kLdsXchg = kPairs * kLdsPair;     // score exchange: [wave][lane] f32x4
+constexpr int kLdsMain = kLdsXchg + 2 * kWaves * 64 * 16;   // double-buffered exchange
+constexpr int kMergeFrag = kWaves * 16 * 64 * 16;
+constexpr int kMergeBytes = kMergeFrag + kPairs * 2 * kHeads * 4;
+constexpr int kLdsTotal = (kLdsMain > kMergeBytes) ? kLdsMain : kMergeBytes;
 constexpr float kTau = 8.0f;                    // lazy-rescale threshold (base-2 units)
 constexpr float kNegInf = -__builtin_inff();
 
@@ -91,29 +98,87 @@ __device__ __forceinline__ int scale_pos(int row) {
 //  * rows: 19 slots per row (18 data + 1 pad), row stride 304 bytes;
 //  * scales: slot (pair q, position pos) holds the E8M0 bytes of blocks 2q
 //    and 2q+1 of the token at `pos` (scale_pos order).
-__device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
-                                          const uint8_t* __restrict__ sc, int t0, int ke,
-                                          int lane) {
+// Per-lane byte offsets of this wave's DMA slots relative to the tile's
+// first token (identical for every full tile, so computed once).
+struct DmaLanes {
+  uint32_t row_off[(kRowDma + 1) / 2];    // 288*row + 16*chunk
+  uint32_t row_idx[(kRowDma + 1) / 2];    // row of the slot (tile-relative token)
+  uint32_t row_chunk[(kRowDma + 1) / 2];
+  uint32_t sc_off[(kScaleDma + 1) / 2];   // 18*row + 2*pair
+  uint32_t sc_idx[(kScaleDma + 1) / 2];
+  uint32_t sc_pair[(kScaleDma + 1) / 2];
+};
+
+__device__ __forceinline__ DmaLanes dma_lanes(int lane, int half) {
+  DmaLanes d;
 #pragma unroll
-  for (int i = 0; i < kRowDma; ++i) {
+  for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
+    const int i = 2 * ii + half;
     const int k = 64 * i + lane;
-    int row = k / 19;
-    int chunk = k - 19 * row;
-    row = min(row, kTile - 1);
-    chunk = min(chunk, 17);
-    const int tok = min(t0 + row, ke - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(kv + (size_t)tok * kRowBytes + 16 * chunk),
-                                     (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+    const int row = min(k / 19, kTile - 1);
+    const int chunk = min(k - 19 * (k / 19), 17);
+    d.row_idx[ii] = row;
+    d.row_chunk[ii] = chunk;
+    d.row_off[ii] = kRowBytes * row + 16 * chunk;
   }
 #pragma unroll
-  for (int i = 0; i < kScaleDma; ++i) {
+  for (int ii = 0; ii < (kScaleDma + 1) / 2; ++ii) {
+    const int i = 2 * ii + half;
     const int slot = min(64 * i + lane, kScaleSlots - 1);
     const int pair = slot >> 5;
     const int pos = slot & 31;
     const int row = 16 * ((pos >> 2) & 1) + 4 * (pos >> 3) + (pos & 3);
-    const int tok = min(t0 + row, ke - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(sc + (size_t)tok * kBlocks + 2 * pair),
-                                     (MLA_LDS void*)(buf + kLdsScale + 256 * i), 2, 0, 0);
+    d.sc_idx[ii] = row;
+    d.sc_pair[ii] = pair;
+    d.sc_off[ii] = kBlocks * row + 2 * pair;
+  }
+  return d;
+}
+
+// Issue this wave's share of the DMA for the tile starting at token t0
+// (`nvalid` = tokens of the tile inside the item; rows past it re-read the
+// item's last token, whose contribution is later multiplied by p = 0).
+__device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
+                                          const uint8_t* __restrict__ sc, int t0, int nvalid,
+                                          const DmaLanes& d, int half) {
+  // t0, nvalid, half and buf are wave-uniform: the tile base goes in SGPRs and
+  // each lane only adds its precomputed 32-bit slot offset.
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const uint8_t* kv_t = kv + (size_t)t0 * kRowBytes;
+  const uint8_t* sc_t = sc + (size_t)t0 * kBlocks;
+  if (nvalid >= kTile) {
+#pragma unroll
+    for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
+      const int i = 2 * ii + half;
+      if (i < kRowDma)
+        __builtin_amdgcn_global_load_lds((const void*)(kv_t + d.row_off[ii]),
+                                         (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+    }
+#pragma unroll
+    for (int ii = 0; ii < (kScaleDma + 1) / 2; ++ii) {
+      const int i = 2 * ii + half;
+      if (i < kScaleDma)
+        __builtin_amdgcn_global_load_lds((const void*)(sc_t + d.sc_off[ii]),
+                                         (MLA_LDS void*)(buf + kLdsScale + 256 * i), 2, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
+      const int i = 2 * ii + half;
+      if (i < kRowDma) {
+        const uint32_t off = kRowBytes * min((int)d.row_idx[ii], nvalid - 1) + 16 * d.row_chunk[ii];
+        __builtin_amdgcn_global_load_lds((const void*)(kv_t + off), (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ii = 0; ii < (kScaleDma + 1) / 2; ++ii) {
+      const int i = 2 * ii + half;
+      if (i < kScaleDma) {
+        const uint32_t off = kBlocks * min((int)d.sc_idx[ii], nvalid - 1) + 2 * d.sc_pair[ii];
+        __builtin_amdgcn_global_load_lds((const void*)(sc_t + off), (MLA_LDS void*)(buf + kLdsScale + 256 * i), 2, 0, 0);
+      }
+    }
   }
 }
 
@@ -125,33 +190,25 @@ __device__ __forceinline__ int scale_byte(int blk, int pos) {
 // LDS reads issued from inline assembly: the compiler does not count them,
 // so their results are only used after an explicit lgkmcnt wait that names
 // the destination registers.
+template <int kOff>
 __device__ __forceinline__ u32x2_t lds_tr8(uint32_t addr) {
   u32x2_t r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
   return r;
 }
+template <int kOff>
 __device__ __forceinline__ u32x4_t lds_b128(uint32_t addr) {
   u32x4_t r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
   return r;
 }
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const MLA_LDS uint8_t*)p;
 }
 
-// Wait until at most `tiles_after` tiles of DMA are still in flight (vector
-// memory operations complete in order). The memory clobber keeps the LDS
-// reads of the tile below this point.
-__device__ __forceinline__ void wait_tiles(int tiles_after) {
-  static_assert(2 * kDmaPerTile < 64, "vmcnt field is 6 bits");
-  if (tiles_after >= 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerTile) : "memory");
-  } else if (tiles_after == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerTile) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-}
+// Wait for this wave's share of the DMA in flight (vector memory operations
+// complete in order). The memory clobber keeps later LDS reads below it.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // 8 e2m1 codes (one dword, low nibble first) times 2^(e-127) -> 8 bf16.
 // The converter reads only the exponent field of the scale operand.
@@ -177,110 +234,138 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 struct WaveState {
-  f32x4_t o[32];     // O fragments: o[2B + parity] covers dims 32B + 2*col + parity
+  f32x4_t o[16];     // O fragments of this half's 8 scale blocks: o[2b + parity]
+  f32x4_t l;         // softmax denominator of heads 4*grp + r (C layout, any column)
   float m;           // running max (base-2 scaled scores) of head `col`
-  float l;           // this lane's share of the softmax denominator
 };
 
-// One 32-token tile of one wave. `buf` holds the staged tile; tokens
-// t0 .. t0+31 (those >= ke are masked).
-__device__ __forceinline__ void process_tile(const uint8_t* buf, int t0, int ke,
-                                             const bf16x8_t (&qf)[18], WaveState& ws,
-                                             float csc, int lane) {
+// Max over the 4 lanes that hold the same head (lanes h, h+16, h+32, h+48).
+__device__ __forceinline__ float max_over_groups(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m1 = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const uint32_t u1 = __builtin_bit_cast(uint32_t, m1);
+  const auto c = __builtin_amdgcn_permlane16_swap(u1, u1, false, false);
+  return fmaxf(__builtin_bit_cast(float, c[0]), __builtin_bit_cast(float, c[1]));
+}
+
+// S^T = K Q^T for one 16-token sub-tile: returns, for head `col`, the raw
+// scores of tokens 16*sub + 4*grp + r (r = 0..3).
+__device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub,
+                                              const bf16x8_t (&qf)[18], int lane) {
   const int col = lane & 15;
   const int grp = lane >> 4;
-
-  // ---- S^T = K Q^T for the two 16-token sub-tiles ----
-  f32x4_t s_acc[2];
+  const int row = 16 * sub + col;
+  const uint8_t* rp = buf + row * kLdsRow;
+  u32x4_t c[4];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int row = 16 * sub + col;
-    const uint8_t* rp = buf + row * kLdsRow;
-    u32x4_t c[4];
+  for (int m = 0; m < 4; ++m) c[m] = *(const u32x4_t*)(rp + 16 * (4 * m + grp));
+  const u32x2_t rope = *(const u32x2_t*)(rp + 256 + 8 * grp);
+  const int pos = scale_pos(row);
+  uint32_t e[5];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) c[m] = *(const u32x4_t*)(rp + 16 * (4 * m + grp));
-    const u32x2_t rope = *(const u32x2_t*)(rp + 256 + 8 * grp);
-    const int pos = scale_pos(row);
-    uint32_t e[5];
+  for (int m = 0; m < 4; ++m) e[m] = buf[scale_byte(4 * m + grp, pos)];
+  e[4] = buf[scale_byte(16 + (grp >> 1), pos)];
+  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) e[m] = buf[scale_byte(4 * m + grp, pos)];
-    e[4] = buf[scale_byte(16 + (grp >> 1), pos)];
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float sc = exp_field(e[m]);
-      a0 = mfma(dequant8(c[m][0], sc), qf[4 * m + 0], a0);
-      a1 = mfma(dequant8(c[m][1], sc), qf[4 * m + 1], a1);
-      a0 = mfma(dequant8(c[m][2], sc), qf[4 * m + 2], a0);
-      a1 = mfma(dequant8(c[m][3], sc), qf[4 * m + 3], a1);
-    }
-    const float sr = exp_field(e[4]);
-    a0 = mfma(dequant8(rope[0], sr), qf[16], a0);
-    a1 = mfma(dequant8(rope[1], sr), qf[17], a1);
-    s_acc[sub] = a0 + a1;
+  for (int m = 0; m < 4; ++m) {
+    const float sc = exp_field(e[m]);
+    a0 = mfma(dequant8(c[m][0], sc), qf[4 * m + 0], a0);
+    a1 = mfma(dequant8(c[m][1], sc), qf[4 * m + 1], a1);
+    a0 = mfma(dequant8(c[m][2], sc), qf[4 * m + 2], a0);
+    a1 = mfma(dequant8(c[m][3], sc), qf[4 * m + 3], a1);
   }
+  const float sr = exp_field(e[4]);
+  a0 = mfma(dequant8(rope[0], sr), qf[16], a0);
+  a1 = mfma(dequant8(rope[1], sr), qf[17], a1);
+  return a0 + a1;
+}
 
-  // ---- online softmax (base 2); lane holds head `col`, tokens 4*grp+r ----
-  float x[8];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
+// Online-softmax update with the scores of the whole 32-token tile (s0: sub-
+// tile 0, s1: sub-tile 1) and O += P V over this half's scale blocks
+// 8*half .. 8*half+7. Both waves of a pair run the softmax on identical data,
+// so their (m, l, P) agree exactly.
+__device__ __forceinline__ void softmax_pv(const uint8_t* buf, int t0, int ke, f32x4_t s0,
+                                           f32x4_t s1, WaveState& ws, float csc, int lane,
+                                           int half) {
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  if (t0 + kTile > ke) {   // tail tile: mask tokens past the item
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tok = t0 + 16 * sub + 4 * grp + r;
-      x[4 * sub + r] = tok < ke ? s_acc[sub][r] * csc : kNegInf;
+      if (t0 + 4 * grp + r >= ke) x[r] = kNegInf;
+      if (t0 + 16 + 4 * grp + r >= ke) x[4 + r] = kNegInf;
     }
+  }
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                    fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_over_groups(mx) * csc;
   const bool need = mx > ws.m + kTau;
   if (__ballot(need)) {
     const float m_new = need ? mx : ws.m;
     const float alpha = need ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;
-    ws.l *= alpha;
     ws.m = m_new;
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r);
 #pragma unroll
-    for (int n = 0; n < 32; ++n)
+    for (int r = 0; r < 4; ++r) ws.l[r] *= al[r];
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ws.o[n][r] *= al[r];
   }
   const float base = ws.m == kNegInf ? 0.0f : ws.m;
   float p[8];
-  float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(x[i] - base);
-    psum += p[i];
-  }
-  ws.l += psum;
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], csc, -base));
   const bf16x8_t pa = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                        (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+  // l += sum_t P[h][t] of the same bf16-rounded P that multiplies V
+  const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  ws.l = mfma(pa, ones, ws.l);
 
-  // ---- O += P V: V from the packed tile via 8-bit transposing reads ----
+  // P V contracts over (token, dim parity) pairs: the decoded V dword of
+  // token k holds (V[t_k][2j], V[t_k][2j+1]), so the B operand is the
+  // decoder output as is, and P is spread into the even (resp. odd) K slots
+  // of the A operand with zeros in the others. pz[e + 2*g2] covers tokens
+  // 4*g2 .. 4*g2+3 of the lane group for output parity e.
+  const u32x4_t pw = __builtin_bit_cast(u32x4_t, pa);
+  const u32x4_t pz0 = {pw[0] & 0xFFFFu, pw[0] >> 16, pw[1] & 0xFFFFu, pw[1] >> 16};
+  const u32x4_t pz1 = {pw[0] << 16, pw[0] & 0xFFFF0000u, pw[1] << 16, pw[1] & 0xFFFF0000u};
+  const u32x4_t pz2 = {pw[2] & 0xFFFFu, pw[2] >> 16, pw[3] & 0xFFFFu, pw[3] >> 16};
+  const u32x4_t pz3 = {pw[2] << 16, pw[2] & 0xFFFF0000u, pw[3] << 16, pw[3] & 0xFFFF0000u};
+  const bf16x8_t a_e1 = __builtin_bit_cast(bf16x8_t, pz0), a_o1 = __builtin_bit_cast(bf16x8_t, pz1);
+  const bf16x8_t a_e2 = __builtin_bit_cast(bf16x8_t, pz2), a_o2 = __builtin_bit_cast(bf16x8_t, pz3);
+
   // lane (col, grp) supplies row k = col/2 of its group's 8 tokens, bytes
   // 8*(col&1).. of a 16-byte column block; it receives byte (16B + col) of
   // all 8 tokens, in the same token order as p[0..7].
   const int k = col >> 1;
   const int trow = (k < 4) ? (4 * grp + k) : (16 + 4 * grp + (k - 4));
-  const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1));
-  const uint32_t sca = lds_addr(buf + kLdsScale + 32 * grp);
+  const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1)) + 128 * half;
+  const uint32_t sca = lds_addr(buf + kLdsScale + 32 * grp) + 4 * kTile * 4 * half;
   // Per pair q of scale blocks: two transposing reads (blocks 2q, 2q+1) and
   // the 8 tokens' scale slots (32 bytes). One pair is in flight while the
   // previous one is decoded.
-  u32x2_t v_cur0 = lds_tr8(tra), v_cur1 = lds_tr8(tra + 16);
-  u32x4_t s_cur0 = lds_b128(sca), s_cur1 = lds_b128(sca + 16);
+  u32x2_t v_cur0 = lds_tr8<0>(tra), v_cur1 = lds_tr8<16>(tra);
+  u32x4_t s_cur0 = lds_b128<0>(sca), s_cur1 = lds_b128<16>(sca);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < 4; ++q) {
     u32x2_t v_nx0, v_nx1;
     u32x4_t s_nx0, s_nx1;
-    if (q < 7) {
-      v_nx0 = lds_tr8(tra + 32 * (q + 1));
-      v_nx1 = lds_tr8(tra + 32 * (q + 1) + 16);
-      s_nx0 = lds_b128(sca + kTile * 4 * (q + 1));
-      s_nx1 = lds_b128(sca + kTile * 4 * (q + 1) + 16);
+    if (q < 3) {
+      constexpr int kTrStep = 32, kScStep = kTile * 4;
+      switch (q) {
+        case 0: v_nx0 = lds_tr8<kTrStep>(tra); v_nx1 = lds_tr8<kTrStep + 16>(tra);
+                s_nx0 = lds_b128<kScStep>(sca); s_nx1 = lds_b128<kScStep + 16>(sca); break;
+        case 1: v_nx0 = lds_tr8<2 * kTrStep>(tra); v_nx1 = lds_tr8<2 * kTrStep + 16>(tra);
+                s_nx0 = lds_b128<2 * kScStep>(sca); s_nx1 = lds_b128<2 * kScStep + 16>(sca); break;
+        default: v_nx0 = lds_tr8<3 * kTrStep>(tra); v_nx1 = lds_tr8<3 * kTrStep + 16>(tra);
+                 s_nx0 = lds_b128<3 * kScStep>(sca); s_nx1 = lds_b128<3 * kScStep + 16>(sca); break;
+      }
       asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(v_cur0), "+v"(v_cur1), "+v"(s_cur0), "+v"(s_cur1));
     } else {
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v_cur0), "+v"(v_cur1), "+v"(s_cur0), "+v"(s_cur1));
@@ -288,11 +373,11 @@ __device__ __forceinline__ void process_tile(const uint8_t* buf, int t0, int ke,
     const uint32_t sv[8] = {s_cur0[0], s_cur0[1], s_cur0[2], s_cur0[3],
                             s_cur1[0], s_cur1[1], s_cur1[2], s_cur1[3]};
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int blk = 2 * q + half;
-      const u32x2_t v = half ? v_cur1 : v_cur0;
-      // token k's scale is byte `half` of slot k: move it to bits 23..30
-      const int sh = half ? 15 : 23;
+    for (int hb = 0; hb < 2; ++hb) {
+      const int lb = 2 * q + hb;             // block within this half
+      const u32x2_t v = hb ? v_cur1 : v_cur0;
+      // token k's scale is byte `hb` of slot k: move it to bits 23..30
+      const int sh = hb ? 15 : 23;
       uint32_t c[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
@@ -307,15 +392,13 @@ __device__ __forceinline__ void process_tile(const uint8_t* buf, int t0, int ke,
         }
         c[kk] = __builtin_bit_cast(uint32_t, cv);
       }
-      // c[k] = (V[t_k][2j], V[t_k][2j+1]); regroup into token pairs per dim
-      const u32x4_t ev = {__builtin_amdgcn_perm(c[1], c[0], 0x05040100u), __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
-                          __builtin_amdgcn_perm(c[5], c[4], 0x05040100u), __builtin_amdgcn_perm(c[7], c[6], 0x05040100u)};
-      const u32x4_t od = {__builtin_amdgcn_perm(c[1], c[0], 0x07060302u), __builtin_amdgcn_perm(c[3], c[2], 0x07060302u),
-                          __builtin_amdgcn_perm(c[5], c[4], 0x07060302u), __builtin_amdgcn_perm(c[7], c[6], 0x07060302u)};
-      ws.o[2 * blk] = mfma(pa, __builtin_bit_cast(bf16x8_t, ev), ws.o[2 * blk]);
-      ws.o[2 * blk + 1] = mfma(pa, __builtin_bit_cast(bf16x8_t, od), ws.o[2 * blk + 1]);
+      const u32x4_t b1 = {c[0], c[1], c[2], c[3]};
+      const u32x4_t b2 = {c[4], c[5], c[6], c[7]};
+      const bf16x8_t vb1 = __builtin_bit_cast(bf16x8_t, b1), vb2 = __builtin_bit_cast(bf16x8_t, b2);
+      ws.o[2 * lb] = mfma(a_e2, vb2, mfma(a_e1, vb1, ws.o[2 * lb]));
+      ws.o[2 * lb + 1] = mfma(a_o2, vb2, mfma(a_o1, vb1, ws.o[2 * lb + 1]));
     }
-    if (q < 7) {
+    if (q < 3) {
       v_cur0 = v_nx0; v_cur1 = v_nx1; s_cur0 = s_nx0; s_cur1 = s_nx1;
     }
   }
@@ -328,7 +411,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
                   float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const int half = wave >> 2;
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -336,7 +421,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int num_slots = plan[kPwNumSlots];
   const int32_t* slot_indptr = plan + plan[kPwOffSlot];
   const int32_t* items = plan + plan[kPwOffItems];
-  uint8_t* wbuf = lds + wave * kLdsWave;
+  uint8_t* ring = lds + pair * kLdsPair;
+  f32x4_t* xchg = (f32x4_t*)(lds + kLdsXchg);
+  const DmaLanes dl = dma_lanes(lane, half);
 
   for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
     const int i_begin = slot_indptr[slot];
@@ -362,70 +449,91 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 
       WaveState ws;
 #pragma unroll
-      for (int n = 0; n < 32; ++n) ws.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < 16; ++n) ws.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      ws.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
       ws.m = kNegInf;
-      ws.l = 0.f;
 
       __syncthreads();  // LDS of the previous item's merge is free again
-      const int t_first = kb + kTile * wave;
+      const int len = ke - kb;
+      const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
+      const int t_first = kb + kTile * pair;
       const int ntiles = t_first < ke ? (ke - t_first + kTileStride - 1) / kTileStride : 0;
-#pragma unroll
-      for (int j = 0; j < kDepth; ++j)
-        if (j < ntiles) stage_dma(wbuf + j * kLdsBuf, kv, sc, t_first + j * kTileStride, ke, lane);
-      for (int i = 0; i < ntiles; ++i) {
-        const int t0 = t_first + i * kTileStride;
-        if (i + kDepth < ntiles)
-          stage_dma(wbuf + ((i + kDepth) % kNumBuf) * kLdsBuf, kv, sc, t0 + kDepth * kTileStride, ke, lane);
-        wait_tiles(min(kDepth, ntiles - 1 - i));
-        process_tile(wbuf + (i % kNumBuf) * kLdsBuf, t0, ke, qf, ws, csc, lane);
+      if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, dl, half);
+      // Round i: QK of tile i and P V of tile i-1 (whose scores the two
+      // halves swapped through LDS before this round's barrier). One tile is
+      // in flight while a round computes. Every wave runs all rounds (the
+      // barrier is workgroup-wide); a pair whose range is exhausted only syncs.
+      f32x4_t s_prev = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i <= rounds; ++i) {
+        const bool qk_on = i < ntiles;
+        const bool pv_on = i >= 1 && i - 1 < ntiles;
+        if (qk_on) wait_dma();
+        __syncthreads();  // tile i landed in both halves; tile i-2 fully consumed; scores of i-1 visible
+        if (i + 1 < ntiles) {
+          const int tn = t_first + (i + 1) * kTileStride;
+          stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, dl, half);
+        }
+        if (pv_on) {
+          const int tp = t_first + (i - 1) * kTileStride;
+          const f32x4_t s_other = xchg[(((i - 1) & 1) * kWaves + (wave ^ 4)) * 64 + lane];
+          const f32x4_t s0 = half ? s_other : s_prev;
+          const f32x4_t s1 = half ? s_prev : s_other;
+          softmax_pv(ring + ((i - 1) % kNumBuf) * kLdsBuf, tp, ke, s0, s1, ws, csc, lane, half);
+        }
+        if (qk_on) {
+          s_prev = qk_subtile(ring + (i % kNumBuf) * kLdsBuf, half, qf, lane);
+          xchg[((i & 1) * kWaves + wave) * 64 + lane] = s_prev;
+        }
       }
 
-      // ---- merge the 4 waves' states ----
-      ws.l += __shfl_xor(ws.l, 16);
-      ws.l += __shfl_xor(ws.l, 32);
+      // ---- merge the 4 pairs' states (the two halves share m and l) ----
       __syncthreads();
       f32x4_t* frag = (f32x4_t*)lds;
       float* stats = (float*)(lds + kMergeFrag);
 #pragma unroll
-      for (int f = 0; f < 32; ++f) frag[(wave * 32 + f) * 64 + lane] = ws.o[f];
-      if (grp == 0) {
-        stats[(2 * wave) * kHeads + col] = ws.m;
-        stats[(2 * wave + 1) * kHeads + col] = ws.l;
+      for (int f = 0; f < 16; ++f) frag[(wave * 16 + f) * 64 + lane] = ws.o[f];
+      if (half == 0 && grp == 0) stats[(2 * pair) * kHeads + col] = ws.m;
+      if (half == 0 && col == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stats[(2 * pair + 1) * kHeads + 4 * grp + r] = ws.l[r];
       }
       __syncthreads();
 
-      float wgt[4][kWaves];
+      float wgt[4][kPairs];
       float inv[4];
       float lse[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
-        float mw[kWaves], lw[kWaves];
+        float mw[kPairs], lw[kPairs];
         float mmax = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kPairs; ++w) {
           mw[w] = stats[(2 * w) * kHeads + h];
           lw[w] = stats[(2 * w + 1) * kHeads + h];
           if (lw[w] != 0.f) mmax = fmaxf(mmax, mw[w]);
         }
         float lsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kPairs; ++w) {
           wgt[r][w] = lw[w] != 0.f ? __builtin_amdgcn_exp2f(mw[w] - mmax) : 0.f;
           lsum += wgt[r][w] * lw[w];
         }
         inv[r] = lsum != 0.f ? 1.0f / lsum : 0.f;
         lse[r] = lsum != 0.f ? mmax + __builtin_amdgcn_logf(lsum) : kNegInf;
       }
-      // wave w handles scale blocks 4w .. 4w+3 (both dim parities)
+      // wave w handles scale blocks 2w, 2w+1 (both dim parities)
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int blk = 4 * wave + bb;
+      for (int bb = 0; bb < 2; ++bb) {
+        const int blk = 2 * wave + bb;
+        const int hb = blk >> 3;      // half that accumulated this block
+        const int lb = blk & 7;
         f32x4_t ev = {0.f, 0.f, 0.f, 0.f}, od = ev;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const f32x4_t fe = frag[(w * 32 + 2 * blk) * 64 + lane];
-          const f32x4_t fo = frag[(w * 32 + 2 * blk + 1) * 64 + lane];
+        for (int w = 0; w < kPairs; ++w) {
+          const int src_wave = w + 4 * hb;
+          const f32x4_t fe = frag[(src_wave * 16 + 2 * lb) * 64 + lane];
+          const f32x4_t fo = frag[(src_wave * 16 + 2 * lb + 1) * 64 + lane];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             ev[r] += wgt[r][w] * fe[r];
@@ -453,9 +561,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 }
 
 // LSE-weighted merge of the partials of one sequence (or zero fill of an
-// empty one). One workgroup per reduce entry; wave w handles heads 4w..4w+3;
-// lane covers 8 consecutive output dims.
-__global__ void __launch_bounds__(kThreads)
+// empty one). One 4-wave workgroup per reduce entry; wave w handles heads
+// 4w..4w+3; lane covers 8 consecutive output dims.
+constexpr int kReduceThreads = 256;
+static_assert(kReduceThreads / 64 * 4 == kHeads, "reduce: 4 heads per wave cover all heads");
+
+__global__ void __launch_bounds__(kReduceThreads)
 mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
                   const float* __restrict__ part_out, uint16_t* __restrict__ out) {
   const int e = blockIdx.x;
@@ -506,7 +617,7 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 
 int launch_reduce(const DecodeArgs& a, void* stream) {
   if (a.num_reduce <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce), dim3(kThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce), dim3(kReduceThreads), 0, (hipStream_t)stream,
                      a.plan, a.part_lse, a.part_out, (uint16_t*)a.out);
   return (int)hipGetLastError();
 }
