@@ -11,6 +11,7 @@ the CPU oracle timed on a bounded sample as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -23,6 +24,47 @@ import torch
 from mla_mxfp4_kv_amd import binding, synth
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel source
+    (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes: int, reps: int) -> int:
+    """Plain device-to-device copy of a known size (calibrates the
+    FETCH_SIZE / WRITE_SIZE counters against bytes actually moved)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+    return 0
 QO_BYTES_PER_SEQ = 16 * 576 * 2 + 16 * 512 * 2
 PARTIAL_BYTES = 16 * (512 + 1) * 4
 
@@ -86,6 +128,8 @@ def main(argv=None):
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
                     help="flush the L2/MALL with a 1 GB write before every timed call")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -95,6 +139,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a HIP GPU", file=sys.stderr)
         return 2
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, max(1, args.steps))
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -183,9 +229,10 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_source_sha256": kernel_source_hash(),
         },
         "cpu_baseline": cpu,
     }

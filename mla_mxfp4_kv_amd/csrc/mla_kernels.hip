@@ -561,45 +561,82 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 }
 
 // LSE-weighted merge of the partials of one sequence (or zero fill of an
-// empty one). One 4-wave workgroup per reduce entry; wave w handles heads
-// 4w..4w+3; lane covers 8 consecutive output dims.
-constexpr int kReduceThreads = 256;
-static_assert(kReduceThreads / 64 * 4 == kHeads, "reduce: 4 heads per wave cover all heads");
+// empty one): out = sum_p 2^(lse_p - M) O_p / sum_p 2^(lse_p - M) with
+// M = max_p lse_p over non-empty partials. One workgroup per (reduce entry,
+// head, quarter of the 512 dims); its 16 waves take every 16th partial (so
+// a long split sequence is merged by many waves with their loads in flight)
+// and are summed through LDS. Lane covers 2 consecutive output dims.
+constexpr int kReduceWaves = 16;
+constexpr int kReduceThreads = 64 * kReduceWaves;
+constexpr int kReduceSplit = 4;                      // dim quarters per head
+static_assert(kVDim / kReduceSplit == 2 * 64, "reduce: a wave covers one quarter of the dims");
 
 __global__ void __launch_bounds__(kReduceThreads)
 mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
                   const float* __restrict__ part_out, uint16_t* __restrict__ out) {
-  const int e = blockIdx.x;
-  const int32_t* ent = plan + plan[kPwOffReduce] + 4 * e;
+  __shared__ f32x2_t acc_s[kReduceWaves][64];
+  __shared__ float wsum_s[kReduceWaves];
+  __shared__ float max_s[kReduceWaves];
+  const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
   const int b = ent[0];
   const int first = ent[1];
   const int cnt = ent[2];
+  const int h = blockIdx.y;
+  const int d = (kVDim / kReduceSplit) * blockIdx.z + 2 * (threadIdx.x & 63);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-#pragma unroll 1
-  for (int hh = 0; hh < 4; ++hh) {
-    const int h = 4 * wave + hh;
-    float mmax = kNegInf;
-    for (int i = 0; i < cnt; ++i) {
-      const float v = part_lse[(size_t)(first + i) * kHeads + h];
-      if (v != kNegInf) mmax = fmaxf(mmax, v);
+  uint32_t* dst = (uint32_t*)(out + ((size_t)b * kHeads + h) * kVDim + d);
+  if (cnt == 0) {
+    if (wave == 0) *dst = 0u;
+    return;
+  }
+  // pass 1: M over non-empty partials
+  float m = kNegInf;
+  for (int i = threadIdx.x; i < cnt; i += kReduceThreads) {
+    const float v = part_lse[(size_t)(first + i) * kHeads + h];
+    if (v != kNegInf) m = fmaxf(m, v);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) max_s[wave] = m;
+  __syncthreads();
+  m = max_s[0];
+#pragma unroll
+  for (int w = 1; w < kReduceWaves; ++w) m = fmaxf(m, max_s[w]);
+  // pass 2: this wave's partials
+  f32x2_t acc = {0.f, 0.f};
+  float wsum = 0.f;
+  for (int i0 = wave; i0 < cnt; i0 += 4 * kReduceWaves) {
+    float v[4];
+    f32x2_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + u * kReduceWaves, cnt - 1);
+      v[u] = part_lse[(size_t)(first + i) * kHeads + h];
+      o[u] = *(const f32x2_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + d);
     }
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-    float wsum = 0.f;
-    for (int i = 0; i < cnt; ++i) {
-      const float v = part_lse[(size_t)(first + i) * kHeads + h];
-      if (v == kNegInf) continue;
-      const float w = __builtin_amdgcn_exp2f(v - mmax);
-      wsum += w;
-      const f32x4_t* src = (const f32x4_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + 8 * lane);
-      a0 += w * src[0];
-      a1 += w * src[1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u * kReduceWaves < cnt && v[u] != kNegInf) {
+        const float w = __builtin_amdgcn_exp2f(v[u] - m);
+        wsum += w;
+        acc += w * o[u];
+      }
     }
-    const float inv = wsum != 0.f ? 1.0f / wsum : 0.f;
-    a0 *= inv;
-    a1 *= inv;
-    const u32x4_t pk = {pack2(a0[0], a0[1]), pack2(a0[2], a0[3]), pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
-    *(u32x4_t*)(out + ((size_t)b * kHeads + h) * kVDim + 8 * lane) = pk;
+  }
+  acc_s[wave][lane] = acc;
+  if (lane == 0) wsum_s[wave] = wsum;
+  __syncthreads();
+  if (wave == 0) {
+    f32x2_t tot = acc_s[0][lane];
+    float ws = wsum_s[0];
+#pragma unroll
+    for (int w = 1; w < kReduceWaves; ++w) {
+      tot += acc_s[w][lane];
+      ws += wsum_s[w];
+    }
+    const float inv = ws != 0.f ? 1.0f / ws : 0.f;
+    *dst = pack2(tot[0] * inv, tot[1] * inv);
   }
 }
 
@@ -617,7 +654,8 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 
 int launch_reduce(const DecodeArgs& a, void* stream) {
   if (a.num_reduce <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce), dim3(kReduceThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce, kHeads, kReduceSplit), dim3(kReduceThreads), 0,
+                     (hipStream_t)stream,
                      a.plan, a.part_lse, a.part_out, (uint16_t*)a.out);
   return (int)hipGetLastError();
 }
