@@ -423,6 +423,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int32_t* items = plan + plan[kPwOffItems];
   uint8_t* ring = lds + pair * kLdsPair;
   f32x4_t* xchg = (f32x4_t*)(lds + kLdsXchg);
+  // The two waves sharing a SIMD run the same instruction stream; giving
+  // one of them issue priority staggers them within a round.
+  if (half) __builtin_amdgcn_s_setprio(1);
   const DmaLanes dl = dma_lanes(lane, half);
 
   for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
