@@ -50,6 +50,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 #define MLA_LDS __attribute__((address_space(3)))
 
 constexpr int kHeads = MLA_NUM_HEADS;
@@ -249,10 +250,119 @@ __device__ __forceinline__ float max_over_groups(float v) {
   return fmaxf(__builtin_bit_cast(float, c[0]), __builtin_bit_cast(float, c[1]));
 }
 
+// Q of one sequence in the operand forms of S^T = K Q^T (lane: head `col`,
+// lane group `grp`).
+//  * Latent dims 0..511 feed v_mfma_scale_f32_16x16x128_f8f6f4 with the fp4
+//    K rows as A: lane group g of A holds the 32 consecutive dims
+//    128m + 32g.. of chunk m (one E8M0 block, whose byte is g's A scale).
+//    The matrix core pairs those nibbles with B bytes such that B lane group
+//    g' must hold dims 128m + 16g' + (0..15) and 128m + 64 + 16g' + (0..15),
+//    and B's scale from lane group g' applies to the B values paired with A
+//    group g' -- Q block 128m + 32g'.. . So a lane converts its two 16-value
+//    halves with the scales of blocks g'/2 and 2 + g'/2 and supplies block
+//    g''s scale byte.
+//  * Each bf16 q is split exactly into hi * 2^(sh-127) + lo * 2^(sl-127),
+//    hi and lo e4m3 (a bf16 mantissa has 8 bits, an e4m3 one 4): sh puts the
+//    block max in [128, 256), sl = sh - 4 (clamped at 0). Byte m of sc_hi /
+//    sc_lo holds the supplied sh / sl of chunk m.
+//  * Rope dims 512..575 stay bf16 for v_mfma_f32_16x16x32_bf16.
+struct QOperands {
+  i32x8_t hi[4];
+  i32x8_t lo[4];
+  uint32_t sc_hi, sc_lo;
+  bf16x8_t rope[2];
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+__device__ __forceinline__ int e8m0_for_max(float mx) {
+  const int ef = (int)(__builtin_bit_cast(uint32_t, mx) >> 23);  // biased exponent of the max
+  return min(max(ef - 7, 0), 254);
+}
+
+// 16 floats -> 16 e4m3 hi bytes and 16 e4m3 lo bytes (4 dwords each) on the
+// E8M0 pair (sh, sh - 4 clamped).
+__device__ __forceinline__ void split16(const float* x, int sh, int* hi, int* lo) {
+  const int sl = max(sh - 4, 0);
+  const float inv = __builtin_bit_cast(float, (uint32_t)(254 - sh) << 23);      // 2^(127 - sh)
+  const float up = __builtin_bit_cast(float, (uint32_t)(127 + sh - sl) << 23);  // 2^(sh - sl)
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float h0 = x[4 * d] * inv, h1 = x[4 * d + 1] * inv;
+    const float h2 = x[4 * d + 2] * inv, h3 = x[4 * d + 3] * inv;
+    int hw = __builtin_amdgcn_cvt_pk_fp8_f32(h0, h1, 0, false);
+    hw = __builtin_amdgcn_cvt_pk_fp8_f32(h2, h3, hw, true);
+    const float r0 = __builtin_amdgcn_cvt_f32_fp8(hw, 0), r1 = __builtin_amdgcn_cvt_f32_fp8(hw, 1);
+    const float r2 = __builtin_amdgcn_cvt_f32_fp8(hw, 2), r3 = __builtin_amdgcn_cvt_f32_fp8(hw, 3);
+    int lw = __builtin_amdgcn_cvt_pk_fp8_f32((h0 - r0) * up, (h1 - r1) * up, 0, false);
+    lw = __builtin_amdgcn_cvt_pk_fp8_f32((h2 - r2) * up, (h3 - r3) * up, lw, true);
+    hi[d] = hw;
+    lo[d] = lw;
+  }
+}
+
+__device__ __forceinline__ QOperands load_q(const uint16_t* qh, int grp) {
+  QOperands f;
+  f.sc_hi = 0u;
+  f.sc_lo = 0u;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const u32x4_t* p0 = (const u32x4_t*)(qh + 128 * m + 16 * grp);
+    const u32x4_t* p1 = (const u32x4_t*)(qh + 128 * m + 64 + 16 * grp);
+    const u32x4_t w[4] = {p0[0], p0[1], p1[0], p1[1]};
+    float x[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * v + 2 * k] = bf16_lo(w[v][k]);
+        x[8 * v + 2 * k + 1] = bf16_hi(w[v][k]);
+      }
+    float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      m0 = fmaxf(m0, fabsf(x[k]));
+      m1 = fmaxf(m1, fabsf(x[16 + k]));
+    }
+    // The other half of blocks grp/2 and 2 + grp/2 sits in lane group grp ^ 1.
+    m0 = fmaxf(m0, __shfl_xor(m0, 16));
+    m1 = fmaxf(m1, __shfl_xor(m1, 16));
+    const int s0 = e8m0_for_max(m0);   // block grp/2
+    const int s1 = e8m0_for_max(m1);   // block 2 + grp/2
+    int hi[8], lo[8];
+    split16(x, s0, hi, lo);
+    split16(x + 16, s1, hi + 4, lo + 4);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      f.hi[m][d] = hi[d];
+      f.lo[m][d] = lo[d];
+    }
+    // Block grp's scale: own s0 (grp 0), own s1 (grp 3), else lane group grp ^ 2's.
+    const int o0 = __shfl_xor(s0, 32), o1 = __shfl_xor(s1, 32);
+    const int sup = grp == 0 ? s0 : grp == 3 ? s1 : grp == 1 ? o0 : o1;
+    f.sc_hi |= (uint32_t)sup << (8 * m);
+    f.sc_lo |= (uint32_t)max(sup - 4, 0) << (8 * m);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) f.rope[s] = *(const bf16x8_t*)(qh + 512 + 16 * grp + 8 * s);
+  return f;
+}
+
+// One 128-dim chunk of S^T: A = 32 fp4 dims of the lane's token row with
+// their E8M0 byte, B = the chunk's e4m3 Q part with the scale byte M.
+template <int M>
+__device__ __forceinline__ f32x4_t mx_chunk(const u32x4_t& k, uint32_t k_scale, const i32x8_t& q,
+                                            uint32_t q_scales, f32x4_t acc) {
+  const i32x8_t a = {(int32_t)k[0], (int32_t)k[1], (int32_t)k[2], (int32_t)k[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, q, acc, 4, 0, 0, (int32_t)k_scale, M,
+                                                          (int32_t)q_scales);
+}
+
 // S^T = K Q^T for one 16-token sub-tile: returns, for head `col`, the raw
 // scores of tokens 16*sub + 4*grp + r (r = 0..3).
-__device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub,
-                                              const bf16x8_t (&qf)[18], int lane) {
+__device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub, const QOperands& qo,
+                                              int lane) {
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int row = 16 * sub + col;
@@ -267,17 +377,17 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub,
   for (int m = 0; m < 4; ++m) e[m] = buf[scale_byte(4 * m + grp, pos)];
   e[4] = buf[scale_byte(16 + (grp >> 1), pos)];
   f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float sc = exp_field(e[m]);
-    a0 = mfma(dequant8(c[m][0], sc), qf[4 * m + 0], a0);
-    a1 = mfma(dequant8(c[m][1], sc), qf[4 * m + 1], a1);
-    a0 = mfma(dequant8(c[m][2], sc), qf[4 * m + 2], a0);
-    a1 = mfma(dequant8(c[m][3], sc), qf[4 * m + 3], a1);
-  }
+  a0 = mx_chunk<0>(c[0], e[0], qo.hi[0], qo.sc_hi, a0);
+  a1 = mx_chunk<0>(c[0], e[0], qo.lo[0], qo.sc_lo, a1);
+  a0 = mx_chunk<1>(c[1], e[1], qo.hi[1], qo.sc_hi, a0);
+  a1 = mx_chunk<1>(c[1], e[1], qo.lo[1], qo.sc_lo, a1);
+  a0 = mx_chunk<2>(c[2], e[2], qo.hi[2], qo.sc_hi, a0);
+  a1 = mx_chunk<2>(c[2], e[2], qo.lo[2], qo.sc_lo, a1);
+  a0 = mx_chunk<3>(c[3], e[3], qo.hi[3], qo.sc_hi, a0);
+  a1 = mx_chunk<3>(c[3], e[3], qo.lo[3], qo.sc_lo, a1);
   const float sr = exp_field(e[4]);
-  a0 = mfma(dequant8(rope[0], sr), qf[16], a0);
-  a1 = mfma(dequant8(rope[1], sr), qf[17], a1);
+  a0 = mfma(dequant8(rope[0], sr), qo.rope[0], a0);
+  a1 = mfma(dequant8(rope[1], sr), qo.rope[1], a1);
   return a0 + a1;
 }
 
@@ -439,16 +549,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int ke = min(items[4 * it + 2], seq_hi);
       const int dest = items[4 * it + 3];
 
-      // Q of sequence b as the B operand of S^T = K Q^T: lane (h = col,
-      // grp) holds, for k-step s, the 8 dims this lane group contracts.
-      bf16x8_t qf[18];
-      const uint16_t* qh = q + ((size_t)b * kHeads + col) * kQkDim;
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        qf[s] = *(const bf16x8_t*)(qh + 32 * (4 * (s >> 2) + grp) + 8 * (s & 3));
-#pragma unroll
-      for (int s = 16; s < 18; ++s)
-        qf[s] = *(const bf16x8_t*)(qh + 512 + 16 * grp + 8 * (s - 16));
+      const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp);
 
       WaveState ws;
 #pragma unroll
@@ -484,7 +585,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           softmax_pv(ring + ((i - 1) % kNumBuf) * kLdsBuf, tp, ke, s0, s1, ws, csc, lane, half);
         }
         if (qk_on) {
-          s_prev = qk_subtile(ring + (i % kNumBuf) * kLdsBuf, half, qf, lane);
+          s_prev = qk_subtile(ring + (i % kNumBuf) * kLdsBuf, half, qo, lane);
           xchg[((i & 1) * kWaves + wave) * 64 + lane] = s_prev;
         }
       }
