@@ -66,16 +66,15 @@ constexpr int kTileStride = kPairs * kTile;     // a pair's step through the ran
 constexpr int kNumBuf = 3;                      // LDS tile buffers per pair: P V, QK, in flight
 constexpr int kLdsRow = 304;                    // packed row + one 16-byte pad (19 slots)
 constexpr int kRowDma = 10;                     // 16-byte DMA instructions per tile (640 slots >= 32*19)
-constexpr int kLdsScale = kRowDma * 64 * 16;    // scale slots after the rows
-constexpr int kScalePairs = kBlocks / 2;        // 9 pairs of scale blocks
-constexpr int kScaleSlots = kScalePairs * kTile;            // 288 four-byte slots
-constexpr int kScaleDma = (kScaleSlots + 63) / 64;          // 2-byte DMA instructions (5)
-constexpr int kDmaHalf0 = (kRowDma + 1) / 2 + (kScaleDma + 1) / 2;  // issued by half 0 (8)
-constexpr int kDmaHalf1 = kRowDma / 2 + kScaleDma / 2;              // issued by half 1 (7)
-constexpr int kLdsBuf = kLdsScale + kScaleDma * 64 * 4;
+constexpr int kLdsRaw = kRowDma * 64 * 16;      // raw E8M0 rows of the tile after the packed rows
+constexpr int kRawChunks = (kTile * kBlocks + 15) / 16 + 1;  // 16-byte chunks covering them at any alignment (37)
+constexpr int kLdsBuf = kLdsRaw + kRawChunks * 16 + 48;      // 10880 (multiple of 64)
 constexpr int kLdsPair = kNumBuf * kLdsBuf;
-constexpr int kLdsXchg = kPairs * kLdsPair;     // score exchange: [wave][lane] f32x4
-constexpr int kLdsMain = kLdsXchg + 2 * kWaves * 64 * 16;   // double-buffered exchange
+constexpr int kVBlocks = kVDim / 32;            // 16 scale blocks of V
+constexpr int kFmtTile = kVBlocks * kTile * 4;  // one tile's V scales as exponent-field dwords
+constexpr int kLdsFmt = kPairs * kLdsPair;      // [parity][pair][block][position] dwords
+constexpr int kLdsXchg = kLdsFmt + 2 * kPairs * kFmtTile;   // score exchange: [parity][wave][lane] f32x4
+constexpr int kLdsMain = kLdsXchg + 2 * kWaves * 64 * 16;
 constexpr int kMergeFrag = kWaves * 16 * 64 * 16;
 constexpr int kMergeBytes = kMergeFrag + kPairs * 2 * kHeads * 4;
 constexpr int kLdsTotal = (kLdsMain > kMergeBytes) ? kLdsMain : kMergeBytes;
@@ -84,8 +83,9 @@ constexpr float kNegInf = -__builtin_inff();
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 
-// Position of tile row (token) 16*s + 4*g + r inside a transposed scale row:
-// lane group g finds its 8 tokens (both sub-tiles) in 8 consecutive bytes.
+// Position of tile row (token) 16*s + 4*g + r in a formatted scale row: lane
+// group g finds the scales of its 8 tokens (both sub-tiles) in 8 consecutive
+// dwords. Inverse: row = 16*((pos >> 2) & 1) + 4*(pos >> 3) + (pos & 3).
 __device__ __forceinline__ int scale_pos(int row) {
   return 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
 }
@@ -93,21 +93,19 @@ __device__ __forceinline__ int scale_pos(int row) {
 // Stage one 32-token tile (tokens t0.., those >= ke replaced by token ke-1,
 // whose contribution is later multiplied by p = 0) into an LDS buffer with
 // direct global->LDS loads. A 16-byte DMA instruction writes 64 consecutive
-// 16-byte LDS slots (lane i -> slot i); a 2-byte one writes lane i's two bytes
-// into the low half of 4-byte slot i. Every lane picks the global address
-// that belongs in its slot, so the loads also lay the tile out:
-//  * rows: 19 slots per row (18 data + 1 pad), row stride 304 bytes;
-//  * scales: slot (pair q, position pos) holds the E8M0 bytes of blocks 2q
-//    and 2q+1 of the token at `pos` (scale_pos order).
-// Per-lane byte offsets of this wave's DMA slots relative to the tile's
+// 16-byte LDS slots (lane i -> slot i), and every lane picks the global
+// address that belongs in its slot:
+//  * rows: 19 slots per row (18 data + 1 pad), row stride 304 bytes, ten
+//    instructions per tile (five per wave of the pair);
+//  * scales: the tile's 18-byte E8M0 rows are contiguous in memory; half 1
+//    copies the 16-byte-aligned chunks that cover them (37 lanes), so byte
+//    (row, blk) lands at raw + delta + 18*row + blk with delta = the start's
+//    offset in its chunk. Chunks past the tile's last valid byte repeat the
+//    last one; aligned chunks of valid bytes never cross a page.
+// Per-lane byte offsets of this wave's row slots relative to the tile's
 // first token (identical for every full tile, so computed once).
 struct DmaLanes {
   uint32_t row_off[(kRowDma + 1) / 2];    // 288*row + 16*chunk
-  uint32_t row_idx[(kRowDma + 1) / 2];    // row of the slot (tile-relative token)
-  uint32_t row_chunk[(kRowDma + 1) / 2];
-  uint32_t sc_off[(kScaleDma + 1) / 2];   // 18*row + 2*pair
-  uint32_t sc_idx[(kScaleDma + 1) / 2];
-  uint32_t sc_pair[(kScaleDma + 1) / 2];
 };
 
 __device__ __forceinline__ DmaLanes dma_lanes(int lane, int half) {
@@ -118,36 +116,27 @@ __device__ __forceinline__ DmaLanes dma_lanes(int lane, int half) {
     const int k = 64 * i + lane;
     const int row = min(k / 19, kTile - 1);
     const int chunk = min(k - 19 * (k / 19), 17);
-    d.row_idx[ii] = row;
-    d.row_chunk[ii] = chunk;
     d.row_off[ii] = kRowBytes * row + 16 * chunk;
-  }
-#pragma unroll
-  for (int ii = 0; ii < (kScaleDma + 1) / 2; ++ii) {
-    const int i = 2 * ii + half;
-    const int slot = min(64 * i + lane, kScaleSlots - 1);
-    const int pair = slot >> 5;
-    const int pos = slot & 31;
-    const int row = 16 * ((pos >> 2) & 1) + 4 * (pos >> 3) + (pos & 3);
-    d.sc_idx[ii] = row;
-    d.sc_pair[ii] = pair;
-    d.sc_off[ii] = kBlocks * row + 2 * pair;
   }
   return d;
 }
 
+// Offset of a tile's first scale byte inside its 16-byte chunk.
+__device__ __forceinline__ int raw_delta(const uint8_t* sc, int t0) {
+  return (int)((uintptr_t)(sc + (size_t)t0 * kBlocks) & 15);
+}
+
 // Issue this wave's share of the DMA for the tile starting at token t0
 // (`nvalid` = tokens of the tile inside the item; rows past it re-read the
-// item's last token, whose contribution is later multiplied by p = 0).
+// item's last token).
 __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
                                           const uint8_t* __restrict__ sc, int t0, int nvalid,
-                                          const DmaLanes& d, int half) {
+                                          const DmaLanes& d, int lane, int half) {
   // t0, nvalid, half and buf are wave-uniform: the tile base goes in SGPRs and
   // each lane only adds its precomputed 32-bit slot offset.
   t0 = __builtin_amdgcn_readfirstlane(t0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   const uint8_t* kv_t = kv + (size_t)t0 * kRowBytes;
-  const uint8_t* sc_t = sc + (size_t)t0 * kBlocks;
   if (nvalid >= kTile) {
 #pragma unroll
     for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
@@ -156,36 +145,45 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
         __builtin_amdgcn_global_load_lds((const void*)(kv_t + d.row_off[ii]),
                                          (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
     }
-#pragma unroll
-    for (int ii = 0; ii < (kScaleDma + 1) / 2; ++ii) {
-      const int i = 2 * ii + half;
-      if (i < kScaleDma)
-        __builtin_amdgcn_global_load_lds((const void*)(sc_t + d.sc_off[ii]),
-                                         (MLA_LDS void*)(buf + kLdsScale + 256 * i), 2, 0, 0);
-    }
   } else {
 #pragma unroll
     for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
       const int i = 2 * ii + half;
       if (i < kRowDma) {
-        const uint32_t off = kRowBytes * min((int)d.row_idx[ii], nvalid - 1) + 16 * d.row_chunk[ii];
+        const int row = (int)d.row_off[ii] / kRowBytes;
+        const uint32_t off = d.row_off[ii] - kRowBytes * (row - min(row, nvalid - 1));
         __builtin_amdgcn_global_load_lds((const void*)(kv_t + off), (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
       }
     }
-#pragma unroll
-    for (int ii = 0; ii < (kScaleDma + 1) / 2; ++ii) {
-      const int i = 2 * ii + half;
-      if (i < kScaleDma) {
-        const uint32_t off = kBlocks * min((int)d.sc_idx[ii], nvalid - 1) + 2 * d.sc_pair[ii];
-        __builtin_amdgcn_global_load_lds((const void*)(sc_t + off), (MLA_LDS void*)(buf + kLdsScale + 256 * i), 2, 0, 0);
-      }
-    }
+  }
+  if (half) {
+    const uintptr_t first = (uintptr_t)(sc + (size_t)t0 * kBlocks);
+    const uintptr_t last_chunk = (first + (uintptr_t)(kBlocks * min(nvalid, kTile)) - 1) & ~(uintptr_t)15;
+    const uintptr_t src = min((first & ~(uintptr_t)15) + 16 * (uintptr_t)lane, last_chunk);
+    if (lane < kRawChunks)
+      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
   }
 }
 
-// Byte address of the E8M0 scale of block `blk` for tile row position `pos`.
-__device__ __forceinline__ int scale_byte(int blk, int pos) {
-  return kLdsScale + (blk >> 1) * (kTile * 4) + 4 * pos + (blk & 1);
+// Rewrite the V scales of a landed tile as exponent-field dwords (e << 23,
+// the form the fp4 converter takes as its scale operand) into `fmt`
+// ([block][position]): the pair's 128 lanes each take one block and four
+// consecutive positions. Rows at or past `nvalid` get scale 1 (their p is 0,
+// and a stale byte must not turn 0 * V into NaN).
+__device__ __forceinline__ void format_scales(const uint8_t* buf, uint8_t* fmt, int delta,
+                                              int nvalid, int lane, int half) {
+  const int l = 64 * half + lane;
+  const int blk = l >> 3;
+  const int pg = l & 7;
+  const int row0 = 16 * (pg & 1) + 4 * (pg >> 1);
+  const uint8_t* raw = buf + kLdsRaw + delta + blk;
+  u32x4_t v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t e = raw[kBlocks * (row0 + j)];
+    v[j] = row0 + j < nvalid ? e << 23 : 127u << 23;
+  }
+  *(u32x4_t*)(fmt + blk * (kTile * 4) + 16 * pg) = v;
 }
 
 // LDS reads issued from inline assembly: the compiler does not count them,
@@ -361,8 +359,8 @@ __device__ __forceinline__ f32x4_t mx_chunk(const u32x4_t& k, uint32_t k_scale, 
 
 // S^T = K Q^T for one 16-token sub-tile: returns, for head `col`, the raw
 // scores of tokens 16*sub + 4*grp + r (r = 0..3).
-__device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub, const QOperands& qo,
-                                              int lane) {
+__device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int delta, int sub,
+                                              const QOperands& qo, int lane) {
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int row = 16 * sub + col;
@@ -371,11 +369,11 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub, const
 #pragma unroll
   for (int m = 0; m < 4; ++m) c[m] = *(const u32x4_t*)(rp + 16 * (4 * m + grp));
   const u32x2_t rope = *(const u32x2_t*)(rp + 256 + 8 * grp);
-  const int pos = scale_pos(row);
+  const uint8_t* er = buf + kLdsRaw + delta + kBlocks * row;
   uint32_t e[5];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) e[m] = buf[scale_byte(4 * m + grp, pos)];
-  e[4] = buf[scale_byte(16 + (grp >> 1), pos)];
+  for (int m = 0; m < 4; ++m) e[m] = er[4 * m + grp];
+  e[4] = er[16 + (grp >> 1)];
   f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
   a0 = mx_chunk<0>(c[0], e[0], qo.hi[0], qo.sc_hi, a0);
   a1 = mx_chunk<0>(c[0], e[0], qo.lo[0], qo.sc_lo, a1);
@@ -395,9 +393,9 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int sub, const
 // tile 0, s1: sub-tile 1) and O += P V over this half's scale blocks
 // 8*half .. 8*half+7. Both waves of a pair run the softmax on identical data,
 // so their (m, l, P) agree exactly.
-__device__ __forceinline__ void softmax_pv(const uint8_t* buf, int t0, int ke, f32x4_t s0,
-                                           f32x4_t s1, WaveState& ws, float csc, int lane,
-                                           int half) {
+__device__ __forceinline__ void softmax_pv(const uint8_t* buf, const uint8_t* fmt, int t0, int ke,
+                                           f32x4_t s0, f32x4_t s1, WaveState& ws, float csc,
+                                           int lane, int half) {
   const int col = lane & 15;
   const int grp = lane >> 4;
   float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -456,60 +454,54 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* buf, int t0, int ke, f
   const int k = col >> 1;
   const int trow = (k < 4) ? (4 * grp + k) : (16 + 4 * grp + (k - 4));
   const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1)) + 128 * half;
-  const uint32_t sca = lds_addr(buf + kLdsScale + 32 * grp) + 4 * kTile * 4 * half;
-  // Per pair q of scale blocks: two transposing reads (blocks 2q, 2q+1) and
-  // the 8 tokens' scale slots (32 bytes). One pair is in flight while the
-  // previous one is decoded.
-  u32x2_t v_cur0 = lds_tr8<0>(tra), v_cur1 = lds_tr8<16>(tra);
-  u32x4_t s_cur0 = lds_b128<0>(sca), s_cur1 = lds_b128<16>(sca);
+  // the 8 tokens' formatted scales of block (8*half + lb): 32 bytes
+  const uint32_t sca = lds_addr(fmt + 32 * grp) + 8 * half * (kTile * 4);
+  // Per block: one transposing read and two scale reads; the next block's
+  // reads are in flight while this one is decoded.
+  u32x2_t v_cur = lds_tr8<0>(tra);
+  u32x4_t s_lo = lds_b128<0>(sca), s_hi = lds_b128<16>(sca);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    u32x2_t v_nx0, v_nx1;
-    u32x4_t s_nx0, s_nx1;
-    if (q < 3) {
-      constexpr int kTrStep = 32, kScStep = kTile * 4;
-      switch (q) {
-        case 0: v_nx0 = lds_tr8<kTrStep>(tra); v_nx1 = lds_tr8<kTrStep + 16>(tra);
-                s_nx0 = lds_b128<kScStep>(sca); s_nx1 = lds_b128<kScStep + 16>(sca); break;
-        case 1: v_nx0 = lds_tr8<2 * kTrStep>(tra); v_nx1 = lds_tr8<2 * kTrStep + 16>(tra);
-                s_nx0 = lds_b128<2 * kScStep>(sca); s_nx1 = lds_b128<2 * kScStep + 16>(sca); break;
-        default: v_nx0 = lds_tr8<3 * kTrStep>(tra); v_nx1 = lds_tr8<3 * kTrStep + 16>(tra);
-                 s_nx0 = lds_b128<3 * kScStep>(sca); s_nx1 = lds_b128<3 * kScStep + 16>(sca); break;
-      }
-      asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(v_cur0), "+v"(v_cur1), "+v"(s_cur0), "+v"(s_cur1));
+  for (int lb = 0; lb < 8; ++lb) {
+    u32x2_t v_nx;
+    u32x4_t s_nlo, s_nhi;
+    constexpr int kScStep = kTile * 4;
+    switch (lb) {
+      case 0: v_nx = lds_tr8<16>(tra); s_nlo = lds_b128<kScStep>(sca); s_nhi = lds_b128<kScStep + 16>(sca); break;
+      case 1: v_nx = lds_tr8<32>(tra); s_nlo = lds_b128<2 * kScStep>(sca); s_nhi = lds_b128<2 * kScStep + 16>(sca); break;
+      case 2: v_nx = lds_tr8<48>(tra); s_nlo = lds_b128<3 * kScStep>(sca); s_nhi = lds_b128<3 * kScStep + 16>(sca); break;
+      case 3: v_nx = lds_tr8<64>(tra); s_nlo = lds_b128<4 * kScStep>(sca); s_nhi = lds_b128<4 * kScStep + 16>(sca); break;
+      case 4: v_nx = lds_tr8<80>(tra); s_nlo = lds_b128<5 * kScStep>(sca); s_nhi = lds_b128<5 * kScStep + 16>(sca); break;
+      case 5: v_nx = lds_tr8<96>(tra); s_nlo = lds_b128<6 * kScStep>(sca); s_nhi = lds_b128<6 * kScStep + 16>(sca); break;
+      case 6: v_nx = lds_tr8<112>(tra); s_nlo = lds_b128<7 * kScStep>(sca); s_nhi = lds_b128<7 * kScStep + 16>(sca); break;
+      default: break;
+    }
+    if (lb < 7) {
+      asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(v_cur), "+v"(s_lo), "+v"(s_hi));
     } else {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v_cur0), "+v"(v_cur1), "+v"(s_cur0), "+v"(s_cur1));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v_cur), "+v"(s_lo), "+v"(s_hi));
     }
-    const uint32_t sv[8] = {s_cur0[0], s_cur0[1], s_cur0[2], s_cur0[3],
-                            s_cur1[0], s_cur1[1], s_cur1[2], s_cur1[3]};
+    const uint32_t sv[8] = {s_lo[0], s_lo[1], s_lo[2], s_lo[3], s_hi[0], s_hi[1], s_hi[2], s_hi[3]};
+    uint32_t c[8];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int lb = 2 * q + hb;             // block within this half
-      const u32x2_t v = hb ? v_cur1 : v_cur0;
-      // token k's scale is byte `hb` of slot k: move it to bits 23..30
-      const int sh = hb ? 15 : 23;
-      uint32_t c[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const float scl = __builtin_bit_cast(float, sv[kk] << sh);
-        const uint32_t src = kk < 4 ? v[0] : v[1];
-        bf16x2_t cv;
-        switch (kk & 3) {
-          case 0: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0); break;
-          case 1: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1); break;
-          case 2: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2); break;
-          default: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3); break;
-        }
-        c[kk] = __builtin_bit_cast(uint32_t, cv);
+    for (int kk = 0; kk < 8; ++kk) {
+      const float scl = __builtin_bit_cast(float, sv[kk]);
+      const uint32_t src = kk < 4 ? v_cur[0] : v_cur[1];
+      bf16x2_t cv;
+      switch (kk & 3) {
+        case 0: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0); break;
+        case 1: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1); break;
+        case 2: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2); break;
+        default: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3); break;
       }
-      const u32x4_t b1 = {c[0], c[1], c[2], c[3]};
-      const u32x4_t b2 = {c[4], c[5], c[6], c[7]};
-      const bf16x8_t vb1 = __builtin_bit_cast(bf16x8_t, b1), vb2 = __builtin_bit_cast(bf16x8_t, b2);
-      ws.o[2 * lb] = mfma(a_e2, vb2, mfma(a_e1, vb1, ws.o[2 * lb]));
-      ws.o[2 * lb + 1] = mfma(a_o2, vb2, mfma(a_o1, vb1, ws.o[2 * lb + 1]));
+      c[kk] = __builtin_bit_cast(uint32_t, cv);
     }
-    if (q < 3) {
-      v_cur0 = v_nx0; v_cur1 = v_nx1; s_cur0 = s_nx0; s_cur1 = s_nx1;
+    const u32x4_t b1 = {c[0], c[1], c[2], c[3]};
+    const u32x4_t b2 = {c[4], c[5], c[6], c[7]};
+    const bf16x8_t vb1 = __builtin_bit_cast(bf16x8_t, b1), vb2 = __builtin_bit_cast(bf16x8_t, b2);
+    ws.o[2 * lb] = mfma(a_e2, vb2, mfma(a_e1, vb1, ws.o[2 * lb]));
+    ws.o[2 * lb + 1] = mfma(a_o2, vb2, mfma(a_o1, vb1, ws.o[2 * lb + 1]));
+    if (lb < 7) {
+      v_cur = v_nx; s_lo = s_nlo; s_hi = s_nhi;
     }
   }
 }
@@ -533,6 +525,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int32_t* items = plan + plan[kPwOffItems];
   uint8_t* ring = lds + pair * kLdsPair;
   f32x4_t* xchg = (f32x4_t*)(lds + kLdsXchg);
+  uint8_t* fmt_pair = lds + kLdsFmt + pair * kFmtTile;  // + parity * kPairs * kFmtTile
   // The two waves sharing a SIMD run the same instruction stream; giving
   // one of them issue priority staggers them within a round.
   if (half) __builtin_amdgcn_s_setprio(1);
@@ -562,7 +555,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
       const int t_first = kb + kTile * pair;
       const int ntiles = t_first < ke ? (ke - t_first + kTileStride - 1) / kTileStride : 0;
-      if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, dl, half);
+      if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, dl, lane, half);
       // Round i: QK of tile i and P V of tile i-1 (whose scores the two
       // halves swapped through LDS before this round's barrier). One tile is
       // in flight while a round computes. Every wave runs all rounds (the
@@ -575,17 +568,23 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         __syncthreads();  // tile i landed in both halves; tile i-2 fully consumed; scores of i-1 visible
         if (i + 1 < ntiles) {
           const int tn = t_first + (i + 1) * kTileStride;
-          stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, dl, half);
+          stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, dl, lane, half);
         }
         if (pv_on) {
           const int tp = t_first + (i - 1) * kTileStride;
           const f32x4_t s_other = xchg[(((i - 1) & 1) * kWaves + (wave ^ 4)) * 64 + lane];
           const f32x4_t s0 = half ? s_other : s_prev;
           const f32x4_t s1 = half ? s_prev : s_other;
-          softmax_pv(ring + ((i - 1) % kNumBuf) * kLdsBuf, tp, ke, s0, s1, ws, csc, lane, half);
+          softmax_pv(ring + ((i - 1) % kNumBuf) * kLdsBuf, fmt_pair + ((i - 1) & 1) * (kPairs * kFmtTile),
+                     tp, ke, s0, s1, ws, csc, lane, half);
         }
         if (qk_on) {
-          s_prev = qk_subtile(ring + (i % kNumBuf) * kLdsBuf, half, qo, lane);
+          const int tq = t_first + i * kTileStride;
+          const uint8_t* bq = ring + (i % kNumBuf) * kLdsBuf;
+          const int dq = raw_delta(sc, tq);
+          s_prev = qk_subtile(bq, dq, half, qo, lane);
+          // V scales of tile i for its P V in the next round
+          format_scales(bq, fmt_pair + (i & 1) * (kPairs * kFmtTile), dq, ke - tq, lane, half);
           xchg[((i & 1) * kWaves + wave) * 64 + lane] = s_prev;
         }
       }
