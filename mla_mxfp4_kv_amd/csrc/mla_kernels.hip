@@ -64,11 +64,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                       // tokens per pair step
 constexpr int kTileStride = kPairs * kTile;     // a pair's step through the range
 constexpr int kNumBuf = 3;                      // LDS tile buffers per pair: P V, QK, in flight
-constexpr int kLdsRow = 304;                    // packed row + one 16-byte pad (19 slots)
-constexpr int kRowDma = 10;                     // 16-byte DMA instructions per tile (640 slots >= 32*19)
-constexpr int kLdsRaw = kRowDma * 64 * 16;      // raw E8M0 rows of the tile after the packed rows
+constexpr int kLdsRow = kRowBytes;              // packed rows as in memory: a tile is one contiguous copy
+constexpr int kRowDma = kTile * kRowBytes / 1024;  // 16-byte DMA instructions per tile (9)
+constexpr int kLdsRaw = kTile * kRowBytes;      // raw E8M0 rows of the tile after the packed rows
 constexpr int kRawChunks = (kTile * kBlocks + 15) / 16 + 1;  // 16-byte chunks covering them at any alignment (37)
-constexpr int kLdsBuf = kLdsRaw + kRawChunks * 16 + 48;      // 10880 (multiple of 64)
+constexpr int kLdsBuf = kLdsRaw + kRawChunks * 16 + 48;      // 9856 (multiple of 64)
 constexpr int kLdsPair = kNumBuf * kLdsBuf;
 constexpr int kVBlocks = kVDim / 32;            // 16 scale blocks of V
 constexpr int kFmtTile = kVBlocks * kTile * 4;  // one tile's V scales as exponent-field dwords
@@ -82,6 +82,7 @@ constexpr float kTau = 8.0f;                    // lazy-rescale threshold (base-
 constexpr float kNegInf = -__builtin_inff();
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
+static_assert(kTile * kRowBytes % 1024 == 0, "a tile's rows are whole 1 KB DMA instructions");
 
 // Position of tile row (token) 16*s + 4*g + r in a formatted scale row: lane
 // group g finds the scales of its 8 tokens (both sub-tiles) in 8 consecutive
@@ -90,79 +91,54 @@ __device__ __forceinline__ int scale_pos(int row) {
   return 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
 }
 
-// Stage one 32-token tile (tokens t0.., those >= ke replaced by token ke-1,
-// whose contribution is later multiplied by p = 0) into an LDS buffer with
-// direct global->LDS loads. A 16-byte DMA instruction writes 64 consecutive
-// 16-byte LDS slots (lane i -> slot i), and every lane picks the global
-// address that belongs in its slot:
-//  * rows: 19 slots per row (18 data + 1 pad), row stride 304 bytes, ten
-//    instructions per tile (five per wave of the pair);
-//  * scales: the tile's 18-byte E8M0 rows are contiguous in memory; half 1
-//    copies the 16-byte-aligned chunks that cover them (37 lanes), so byte
-//    (row, blk) lands at raw + delta + 18*row + blk with delta = the start's
-//    offset in its chunk. Chunks past the tile's last valid byte repeat the
-//    last one; aligned chunks of valid bytes never cross a page.
-// Per-lane byte offsets of this wave's row slots relative to the tile's
-// first token (identical for every full tile, so computed once).
-struct DmaLanes {
-  uint32_t row_off[(kRowDma + 1) / 2];    // 288*row + 16*chunk
-};
-
-__device__ __forceinline__ DmaLanes dma_lanes(int lane, int half) {
-  DmaLanes d;
-#pragma unroll
-  for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
-    const int i = 2 * ii + half;
-    const int k = 64 * i + lane;
-    const int row = min(k / 19, kTile - 1);
-    const int chunk = min(k - 19 * (k / 19), 17);
-    d.row_off[ii] = kRowBytes * row + 16 * chunk;
-  }
-  return d;
-}
-
+// Stage one 32-token tile into an LDS buffer with direct global->LDS loads
+// (a 16-byte DMA instruction writes 64 consecutive 16-byte LDS slots, lane i
+// -> slot i, each lane choosing its global source):
+//  * rows: the tile's 32 packed rows are one contiguous 9 KB range, copied
+//    as is (row stride 288 bytes) by nine instructions; in a tile that ends
+//    the item, slots past its last valid row repeat that row's last 16
+//    bytes (finite fp4 codes; those tokens get p = 0);
+//  * scales: the tile's 18-byte E8M0 rows are contiguous too; the 16-byte-
+//    aligned chunks that cover them are copied (37 lanes), so byte (row,
+//    blk) lands at raw + delta + 18*row + blk with delta = the start's
+//    offset in its chunk. Chunks past the last valid byte repeat the last
+//    one; aligned chunks of valid bytes never cross a page.
+// Only the second wave of the pair issues them: issued by all waves at once,
+// the instructions queue in the CU's address unit and stall every issuer,
+// while this wave otherwise waits at the round's barrier for its partner.
 // Offset of a tile's first scale byte inside its 16-byte chunk.
 __device__ __forceinline__ int raw_delta(const uint8_t* sc, int t0) {
   return (int)((uintptr_t)(sc + (size_t)t0 * kBlocks) & 15);
 }
 
-// Issue this wave's share of the DMA for the tile starting at token t0
-// (`nvalid` = tokens of the tile inside the item; rows past it re-read the
-// item's last token).
+// Issue the DMA of the tile starting at token t0 (`nvalid` = tokens of the
+// tile inside the item).
 __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
                                           const uint8_t* __restrict__ sc, int t0, int nvalid,
-                                          const DmaLanes& d, int lane, int half) {
-  // t0, nvalid, half and buf are wave-uniform: the tile base goes in SGPRs and
-  // each lane only adds its precomputed 32-bit slot offset.
+                                          int lane) {
+  // t0 and nvalid are wave-uniform: the tile base goes in SGPRs and each lane
+  // only adds its 32-bit slot offset.
   t0 = __builtin_amdgcn_readfirstlane(t0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   const uint8_t* kv_t = kv + (size_t)t0 * kRowBytes;
+  const uint32_t lane_off = 16 * lane;
   if (nvalid >= kTile) {
 #pragma unroll
-    for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
-      const int i = 2 * ii + half;
-      if (i < kRowDma)
-        __builtin_amdgcn_global_load_lds((const void*)(kv_t + d.row_off[ii]),
-                                         (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
-    }
+    for (int i = 0; i < kRowDma; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(kv_t + 1024 * i + lane_off),
+                                       (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
   } else {
+    const uint32_t last = (uint32_t)(nvalid * kRowBytes - 16);
 #pragma unroll
-    for (int ii = 0; ii < (kRowDma + 1) / 2; ++ii) {
-      const int i = 2 * ii + half;
-      if (i < kRowDma) {
-        const int row = (int)d.row_off[ii] / kRowBytes;
-        const uint32_t off = d.row_off[ii] - kRowBytes * (row - min(row, nvalid - 1));
-        __builtin_amdgcn_global_load_lds((const void*)(kv_t + off), (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
-      }
-    }
+    for (int i = 0; i < kRowDma; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(kv_t + min(1024 * i + lane_off, last)),
+                                       (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
   }
-  if (half) {
-    const uintptr_t first = (uintptr_t)(sc + (size_t)t0 * kBlocks);
-    const uintptr_t last_chunk = (first + (uintptr_t)(kBlocks * min(nvalid, kTile)) - 1) & ~(uintptr_t)15;
-    const uintptr_t src = min((first & ~(uintptr_t)15) + 16 * (uintptr_t)lane, last_chunk);
-    if (lane < kRawChunks)
-      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
-  }
+  const uintptr_t first = (uintptr_t)(sc + (size_t)t0 * kBlocks);
+  const uintptr_t last_chunk = (first + (uintptr_t)(kBlocks * min(nvalid, kTile)) - 1) & ~(uintptr_t)15;
+  const uintptr_t src = min((first & ~(uintptr_t)15) + lane_off, last_chunk);
+  if (lane < kRawChunks)
+    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
 }
 
 // Rewrite the V scales of a landed tile as exponent-field dwords (e << 23,
@@ -529,7 +505,6 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // The two waves sharing a SIMD run the same instruction stream; giving
   // one of them issue priority staggers them within a round.
   if (half) __builtin_amdgcn_s_setprio(1);
-  const DmaLanes dl = dma_lanes(lane, half);
 
   for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
     const int i_begin = slot_indptr[slot];
@@ -555,7 +530,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
       const int t_first = kb + kTile * pair;
       const int ntiles = t_first < ke ? (ke - t_first + kTileStride - 1) / kTileStride : 0;
-      if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, dl, lane, half);
+      if (half && ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
       // Round i: QK of tile i and P V of tile i-1 (whose scores the two
       // halves swapped through LDS before this round's barrier). One tile is
       // in flight while a round computes. Every wave runs all rounds (the
@@ -564,11 +539,11 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       for (int i = 0; i <= rounds; ++i) {
         const bool qk_on = i < ntiles;
         const bool pv_on = i >= 1 && i - 1 < ntiles;
-        if (qk_on) wait_dma();
-        __syncthreads();  // tile i landed in both halves; tile i-2 fully consumed; scores of i-1 visible
-        if (i + 1 < ntiles) {
+        if (half && qk_on) wait_dma();
+        __syncthreads();  // tile i landed; tile i-2 fully consumed; scores of i-1 visible
+        if (half && i + 1 < ntiles) {
           const int tn = t_first + (i + 1) * kTileStride;
-          stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, dl, lane, half);
+          stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, lane);
         }
         if (pv_on) {
           const int tp = t_first + (i - 1) * kTileStride;
