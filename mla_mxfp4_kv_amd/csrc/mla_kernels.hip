@@ -80,16 +80,10 @@ constexpr int kMergeBytes = kMergeFrag + kPairs * 2 * kHeads * 4;
 constexpr int kLdsTotal = (kLdsMain > kMergeBytes) ? kLdsMain : kMergeBytes;
 constexpr float kTau = 8.0f;                    // lazy-rescale threshold (base-2 units)
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kMInit = -1.0e30f;              // running max before the first tile (finite: no inf - inf)
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 static_assert(kTile * kRowBytes % 1024 == 0, "a tile's rows are whole 1 KB DMA instructions");
-
-// Position of tile row (token) 16*s + 4*g + r in a formatted scale row: lane
-// group g finds the scales of its 8 tokens (both sub-tiles) in 8 consecutive
-// dwords. Inverse: row = 16*((pos >> 2) & 1) + 4*(pos >> 3) + (pos & 3).
-__device__ __forceinline__ int scale_pos(int row) {
-  return 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
-}
 
 // Stage one 32-token tile into an LDS buffer with direct global->LDS loads
 // (a 16-byte DMA instruction writes 64 consecutive 16-byte LDS slots, lane i
@@ -151,13 +145,20 @@ __device__ __forceinline__ void format_scales(const uint8_t* buf, uint8_t* fmt, 
   const int l = 64 * half + lane;
   const int blk = l >> 3;
   const int pg = l & 7;
-  const int row0 = 16 * (pg & 1) + 4 * (pg >> 1);
+  // positions 8g..8g+3: the 4 tokens of lane group g in the sub-tile of the
+  // half that reads this block (blk >> 3), 8g+4..8g+7: the other sub-tile's
+  const int row0 = 16 * ((pg & 1) ^ (blk >> 3)) + 4 * (pg >> 1);
   const uint8_t* raw = buf + kLdsRaw + delta + blk;
   u32x4_t v;
+  if (nvalid >= kTile) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t e = raw[kBlocks * (row0 + j)];
-    v[j] = row0 + j < nvalid ? e << 23 : 127u << 23;
+    for (int j = 0; j < 4; ++j) v[j] = (uint32_t)raw[kBlocks * (row0 + j)] << 23;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e = raw[kBlocks * (row0 + j)];
+      v[j] = row0 + j < nvalid ? e << 23 : 127u << 23;
+    }
   }
   *(u32x4_t*)(fmt + blk * (kTile * 4) + 16 * pg) = v;
 }
@@ -213,6 +214,13 @@ struct WaveState {
   f32x4_t l;         // softmax denominator of heads 4*grp + r (C layout, any column)
   float m;           // running max (base-2 scaled scores) of head `col`
 };
+
+// max(a, b, c) in one instruction (maxNum semantics, as fmaxf).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Max over the 4 lanes that hold the same head (lanes h, h+16, h+32, h+48).
 __device__ __forceinline__ float max_over_groups(float v) {
@@ -365,25 +373,27 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int delta, int
   return a0 + a1;
 }
 
-// Online-softmax update with the scores of the whole 32-token tile (s0: sub-
-// tile 0, s1: sub-tile 1) and O += P V over this half's scale blocks
-// 8*half .. 8*half+7. Both waves of a pair run the softmax on identical data,
-// so their (m, l, P) agree exactly.
+// Online-softmax update with the scores of the whole 32-token tile (s_own:
+// this wave's sub-tile `half`, s_oth: the partner's) and O += P V over this
+// half's scale blocks 8*half .. 8*half+7. Token tables are in "own sub-tile
+// first" order (x, p, the transposing reads, the formatted scales), so the
+// two waves of a pair hold the same (m, l) and P up to the order of tokens.
 __device__ __forceinline__ void softmax_pv(const uint8_t* buf, const uint8_t* fmt, int t0, int ke,
-                                           f32x4_t s0, f32x4_t s1, WaveState& ws, float csc,
+                                           f32x4_t s_own, f32x4_t s_oth, WaveState& ws, float csc,
                                            int lane, int half) {
   const int col = lane & 15;
   const int grp = lane >> 4;
-  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  const int own0 = 16 * half + 4 * grp;         // first own / other token of the lane group
+  const int oth0 = 16 * (1 - half) + 4 * grp;
+  float x[8] = {s_own[0], s_own[1], s_own[2], s_own[3], s_oth[0], s_oth[1], s_oth[2], s_oth[3]};
   if (t0 + kTile > ke) {   // tail tile: mask tokens past the item
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (t0 + 4 * grp + r >= ke) x[r] = kNegInf;
-      if (t0 + 16 + 4 * grp + r >= ke) x[4 + r] = kNegInf;
+      if (t0 + own0 + r >= ke) x[r] = kNegInf;
+      if (t0 + oth0 + r >= ke) x[4 + r] = kNegInf;
     }
   }
-  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  float mx = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), fmaxf(x[6], x[7]));
   mx = max_over_groups(mx) * csc;
   const bool need = mx > ws.m + kTau;
   if (__ballot(need)) {
@@ -400,7 +410,7 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* buf, const uint8_t* fm
 #pragma unroll
       for (int r = 0; r < 4; ++r) ws.o[n][r] *= al[r];
   }
-  const float base = ws.m == kNegInf ? 0.0f : ws.m;
+  const float base = ws.m;
   float p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], csc, -base));
@@ -428,7 +438,7 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* buf, const uint8_t* fm
   // 8*(col&1).. of a 16-byte column block; it receives byte (16B + col) of
   // all 8 tokens, in the same token order as p[0..7].
   const int k = col >> 1;
-  const int trow = (k < 4) ? (4 * grp + k) : (16 + 4 * grp + (k - 4));
+  const int trow = (k < 4) ? (own0 + k) : (oth0 + (k - 4));
   const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1)) + 128 * half;
   // the 8 tokens' formatted scales of block (8*half + lb): 32 bytes
   const uint32_t sca = lds_addr(fmt + 32 * grp) + 8 * half * (kTile * 4);
@@ -523,7 +533,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 #pragma unroll
       for (int n = 0; n < 16; ++n) ws.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       ws.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      ws.m = kNegInf;
+      ws.m = kMInit;
 
       __syncthreads();  // LDS of the previous item's merge is free again
       const int len = ke - kb;
@@ -548,10 +558,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         if (pv_on) {
           const int tp = t_first + (i - 1) * kTileStride;
           const f32x4_t s_other = xchg[(((i - 1) & 1) * kWaves + (wave ^ 4)) * 64 + lane];
-          const f32x4_t s0 = half ? s_other : s_prev;
-          const f32x4_t s1 = half ? s_prev : s_other;
           softmax_pv(ring + ((i - 1) % kNumBuf) * kLdsBuf, fmt_pair + ((i - 1) & 1) * (kPairs * kFmtTile),
-                     tp, ke, s0, s1, ws, csc, lane, half);
+                     tp, ke, s_prev, s_other, ws, csc, lane, half);
         }
         if (qk_on) {
           const int tq = t_first + i * kTileStride;
