@@ -17,7 +17,7 @@
  *             token is the low nibble (j even) or high nibble (j odd) of byte
  *             j/2, an OCP e2m1 code ("kernelbot-amd-mixed-mla-608791",
  *             kFp4Lut and the stage-1 tile fill).
- *   kv_scale  uint8 [T, 18]        device, any alignment. E8M0 byte e scales
+ *   kv_scale  uint8 [T, 18]        device, any byte alignment. E8M0 byte e scales
  *             elements 32k..32k+31 by 2^(e-127); e = 255 is NaN
  *             ("kernelbot-amd-mixed-mla-608791", e8m0_to_float).
  *   kv_indptr int32 [B+1]          non-decreasing token offsets of the

@@ -189,8 +189,7 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
     if (q == nullptr || !aligned(q, 16)) return fail(MLA_ERR_INVALID, "q must be non-null and 16-byte aligned");
     if (kv_packed == nullptr || !aligned(kv_packed, 16))
       return fail(MLA_ERR_INVALID, "kv_packed must be non-null and 16-byte aligned");
-    if (kv_scale == nullptr || !aligned(kv_scale, 2))
-      return fail(MLA_ERR_INVALID, "kv_scale must be non-null and 2-byte aligned");
+    if (kv_scale == nullptr) return fail(MLA_ERR_INVALID, "kv_scale must be non-null");
   }
   mla::DecodeArgs a;
   a.q = q;

@@ -225,11 +225,16 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 // Max over the 4 lanes that hold the same head (lanes h, h+16, h+32, h+48).
 __device__ __forceinline__ float max_over_groups(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  // The swap results are copied to scalars before the bit casts: a bit cast
+  // of an element of the builtin's two-element result reads element 0 for
+  // both, which silently turned this reduction into a copy of lane group 0.
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float m1 = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float m1 = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
   const uint32_t u1 = __builtin_bit_cast(uint32_t, m1);
   const auto c = __builtin_amdgcn_permlane16_swap(u1, u1, false, false);
-  return fmaxf(__builtin_bit_cast(float, c[0]), __builtin_bit_cast(float, c[1]));
+  const uint32_t c0 = c[0], c1 = c[1];
+  return fmaxf(__builtin_bit_cast(float, c0), __builtin_bit_cast(float, c1));
 }
 
 // Q of one sequence in the operand forms of S^T = K Q^T (lane: head `col`,

@@ -146,6 +146,78 @@ def test_nan_scale_poisons_only_its_sequence():
     _check(got, want, "nan")
 
 
+def test_scale_rows_at_any_byte_offset():
+    """kv_scale may start at any byte: the tile's E8M0 rows are fetched as the
+    aligned 16-byte chunks that cover them, so the result must not change."""
+    _say("case kv_scale byte offsets")
+    lens = [37, 300, 1, 1025, 64, 0, 95]
+    q, packed, scales, indptr, _ = _small(lens, seed=11)
+    base = _run(q, packed, scales, indptr.tolist(), 5)
+    for off in (1, 2, 7, 15):
+        buf = torch.full((scales.numel() + 64,), 255, dtype=torch.uint8, device="cuda")
+        view = buf[off:off + scales.numel()].view(scales.shape)
+        view.copy_(scales.cuda())
+        got = _run(q, packed, view, indptr.tolist(), 5)
+        assert np.array_equal(got, base), f"kv_scale at byte offset {off}"
+
+
+def test_query_dynamic_range():
+    """Query blocks whose elements span many binades (and exact zeros): the
+    latent product splits each bf16 q into two e4m3 terms on a per-block
+    power-of-two scale."""
+    _say("case query dynamic range")
+    g = torch.Generator().manual_seed(21)
+    lens = [40, 257, 1000]
+    q, packed, scales, indptr, _ = _small(lens, seed=21)
+    mag = torch.exp2(torch.randint(-20, 1, q.shape, generator=g).float())
+    qw = q.float() * mag
+    qw[torch.rand(q.shape, generator=g) < 0.05] = 0.0
+    qw = qw.to(torch.bfloat16)
+    got = _run(qw, packed, scales, indptr.tolist(), 0)
+    want = ref.mla_decode_ref(_qbits(qw), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    _check(got, want, "q dynamic range")
+
+
+def test_nan_query_poisons_only_its_head():
+    _say("case NaN in q")
+    lens = [100, 500]
+    q, packed, scales, indptr, _ = _small(lens, seed=5)
+    q = q.clone()
+    q[1, 6, 300] = float("nan")
+    got = _run(q, packed, scales, indptr.tolist(), 0)
+    assert np.all(np.isnan(got[1, 6]))
+    mask = np.ones(got.shape, dtype=bool)
+    mask[1, 6] = False
+    assert np.all(np.isfinite(got[mask]))
+    want = ref.mla_decode_ref(_qbits(q), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    _check(got, want, "nan q")
+
+
+def test_wide_scale_range():
+    """E8M0 bytes spread over 116..138 per block: the K scales go straight into
+    the scaled MFMA (QK) and through the converter (PV)."""
+    _say("case wide E8M0 range")
+    g = torch.Generator().manual_seed(33)
+    lens = [64, 333, 1500]
+    q, packed, scales, indptr, _ = _small(lens, seed=33)
+    scales = torch.randint(116, 139, scales.shape, generator=g).to(torch.uint8)
+    qs = (q.float() * 0.02).to(torch.bfloat16)
+    got = _run(qs, packed, scales, indptr.tolist(), 0)
+    want = ref.mla_decode_ref(_qbits(qs), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    # |V| reaches 6 * 2^11 here and scores span hundreds of units, so the bf16
+    # rounding of P (relative 2^-9) allows absolute errors of order |V| * 2^-9
+    # where tokens cancel: bound each head's error by its row's magnitude.
+    assert np.array_equal(np.isnan(got), np.isnan(want)), "wide scales: NaN pattern differs"
+    assert np.all(np.isfinite(got))
+    for b in range(got.shape[0]):
+        for h in range(16):
+            g, w = got[b, h], want[b, h]
+            scale = float(np.max(np.abs(w)))
+            assert np.max(np.abs(g - w)) <= ATOL + RTOL * scale, f"wide scales b={b} h={h}"
+            if scale > 0:
+                assert np.linalg.norm(g - w) / np.linalg.norm(w) <= NORMWISE, f"wide scales b={b} h={h} normwise"
+
+
 def test_permutation_invariance():
     _say("case permutation invariance")
     q, packed, scales, indptr, _ = _small([3000], seed=9)
