@@ -1,7 +1,7 @@
 """Exact MXFP4 dequantisation and fp64 absorbed-MLA decode attention.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): a plain, slow CPU
-statement of what the decode computes, used to judge the HIP library.
+statement of what the decode computes, used to check the HIP library.
 
 What is computed, for every sequence b and head h (q_seq_len = 1):
 
