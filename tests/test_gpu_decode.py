@@ -218,6 +218,41 @@ def test_wide_scale_range():
                 assert np.linalg.norm(g - w) / np.linalg.norm(w) <= NORMWISE, f"wide scales b={b} h={h} normwise"
 
 
+def test_hip_graph_capture_replays():
+    """The decode enqueues kernels only (no allocation, sync or memset), so it
+    can be captured in a HIP graph: each replay must reproduce the eager
+    result bit for bit, also after the inputs change in place."""
+    _say("case HIP graph capture")
+    lens = [37, 1025, 0, 300, 2000]
+    q, packed, scales, indptr, _ = _small(lens, seed=9)
+    q, packed, scales = q.cuda(), packed.cuda(), scales.cuda()
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=7)   # splits -> reduce kernel too
+    out = torch.empty(len(lens), 16, 512, dtype=torch.bfloat16, device="cuda")
+    eager = dec(q, packed, scales, out=torch.empty_like(out), sm_scale=SM).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dec(q, packed, scales, out=out, sm_scale=SM)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dec(q, packed, scales, out=out, sm_scale=SM)
+    for rep in range(3):
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+    q.mul_(0.5)
+    eager2 = dec(q, packed, scales, out=torch.empty_like(out), sm_scale=SM).clone()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager2)
+    want = ref.mla_decode_ref(_qbits(q), packed.cpu().numpy(), scales.cpu().numpy(), indptr.numpy(), SM)
+    _check(out.float().cpu().numpy(), want, "graph")
+
+
 def test_permutation_invariance():
     _say("case permutation invariance")
     q, packed, scales, indptr, _ = _small([3000], seed=9)
