@@ -11,27 +11,27 @@
 // Design for CDNA4 (8 waves per workgroup = 2 per SIMD, one workgroup per
 // CU, persistent over the planner's slots):
 //  * The workgroup's KV range is cut into 32-token tiles interleaved over 4
-//    wave pairs; the two waves of a pair (same SIMD) share each tile. Packed rows (288 B) and E8M0
-//    scales (18 B) go straight from HBM into the pair's LDS ring of three
-//    tile buffers with direct global->LDS loads, one tile ahead of the one
-//    being computed: rows padded to 304 B (bank-conflict-free for all reads
-//    below), scales gathered into [block pair][token] slots.
-//  * One workgroup barrier per round: in round i a wave computes QK for
-//    tile i and P V for tile i-1, so independent work interleaves.
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, one 16-token half of the tile
-//    per wave (scores swapped through LDS): A = K rows (lane = token,
-//    decoded in registers by v_cvt_scalef32_pk_bf16_fp4, which is exactly
-//    e2m1 * 2^(e-127)), B = Q^T (16 heads, held in registers for the item).
-//    The 16 heads are the MFMA's N dimension, so every K tile is used by
-//    all heads at once.
-//  * Online softmax in base 2 with a lazily updated running max (rescale
-//    only when a tile max exceeds it by more than 8), cross-lane reductions
-//    over the 4 lane groups.
-//  * O += P V on the same MFMA, each wave of a pair owning 256 of the 512
-//    latent dims (so O fits in 64 registers): V comes from the packed LDS tile through
-//    ds_read_b64_tr_b8 (8 tokens x 1 byte per lane), is decoded with each
-//    token's scale and byte-permuted into token pairs. The even and odd
-//    latent dims of a 32-dim scale block form two output tiles.
+//    wave pairs; the two waves of a pair share a SIMD and each tile, and
+//    split its work by role. Packed rows (288 B, as in memory) and the
+//    E8M0 rows (18 B, as the 16-byte chunks that cover them) go straight
+//    from HBM into the pair's LDS ring of three tile buffers with direct
+//    global->LDS loads, one tile ahead of the one being scored.
+//  * One workgroup barrier per round: in round i the scorer wave computes
+//    S for tile i while the P V wave accumulates tile i-1, so the matrix
+//    core of the SIMD takes one wave's products while the other decodes or
+//    exponentiates.
+//  * Scorer: S^T = K Q^T with the 16 heads as the MFMA's N dimension. The
+//    512 latent dims run on v_mfma_scale_f32_16x16x128_f8f6f4 with the
+//    packed fp4 rows and their E8M0 bytes as the scaled A operand and q as
+//    an exact hi + lo pair of e4m3 operands with per-block scales; the 64
+//    rope dims on v_mfma_f32_16x16x32_bf16 after v_cvt_scalef32_pk_bf16_fp4
+//    (exactly e2m1 * 2^(e-127)). Then the online softmax in base 2 with a
+//    lazily updated running max (rescale only when a tile max exceeds it by
+//    more than 8), and the V scales rewritten as converter operands.
+//  * P V wave: O += P V for all 512 latent dims (O in 128 registers) on the
+//    bf16 MFMA. V comes from the packed LDS tile through ds_read_b64_tr_b8
+//    (8 tokens x 1 byte per lane), is decoded with each token's scale; the
+//    even and odd latent dims of a 32-dim scale block form two output tiles.
 //  * The 4 pairs' (m, l, O) are merged through LDS; a whole-sequence item
 //    writes bf16 output directly, any other item writes a normalised fp32
 //    partial and its base-2 LSE for the reduce kernel.
@@ -73,9 +73,9 @@ constexpr int kLdsPair = kNumBuf * kLdsBuf;
 constexpr int kVBlocks = kVDim / 32;            // 16 scale blocks of V
 constexpr int kFmtTile = kVBlocks * kTile * 4;  // one tile's V scales as exponent-field dwords
 constexpr int kLdsFmt = kPairs * kLdsPair;      // [parity][pair][block][position] dwords
-constexpr int kLdsXchg = kLdsFmt + 2 * kPairs * kFmtTile;   // score exchange: [parity][wave][lane] f32x4
-constexpr int kLdsMain = kLdsXchg + 2 * kWaves * 64 * 16;
-constexpr int kMergeFrag = kWaves * 16 * 64 * 16;
+constexpr int kLdsXchg = kLdsFmt + 2 * kPairs * kFmtTile;   // tile hand-offs: [parity][pair][lane]
+constexpr int kLdsMain = kLdsXchg + 2 * kPairs * 64 * 32;
+constexpr int kMergeFrag = kPairs * 32 * 64 * 16;   // O fragments: [pair][fragment][lane]
 constexpr int kMergeBytes = kMergeFrag + kPairs * 2 * kHeads * 4;
 constexpr int kLdsTotal = (kLdsMain > kMergeBytes) ? kLdsMain : kMergeBytes;
 constexpr float kTau = 8.0f;                    // lazy-rescale threshold (base-2 units)
@@ -97,9 +97,9 @@ static_assert(kTile * kRowBytes % 1024 == 0, "a tile's rows are whole 1 KB DMA i
 //    blk) lands at raw + delta + 18*row + blk with delta = the start's
 //    offset in its chunk. Chunks past the last valid byte repeat the last
 //    one; aligned chunks of valid bytes never cross a page.
-// Only the second wave of the pair issues them: issued by all waves at once,
-// the instructions queue in the CU's address unit and stall every issuer,
-// while this wave otherwise waits at the round's barrier for its partner.
+// Only the pair's scorer issues them (issued by all waves at once, the
+// instructions queue in the CU's address unit and stall every issuer).
+
 // Offset of a tile's first scale byte inside its 16-byte chunk.
 __device__ __forceinline__ int raw_delta(const uint8_t* sc, int t0) {
   return (int)((uintptr_t)(sc + (size_t)t0 * kBlocks) & 15);
@@ -137,17 +137,17 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
 
 // Rewrite the V scales of a landed tile as exponent-field dwords (e << 23,
 // the form the fp4 converter takes as its scale operand) into `fmt`
-// ([block][position]): the pair's 128 lanes each take one block and four
-// consecutive positions. Rows at or past `nvalid` get scale 1 (their p is 0,
-// and a stale byte must not turn 0 * V into NaN).
+// ([block][position]). Position 8g + j of a block is token 4g + j of the
+// first 16-token sub-tile for j < 4 and token 16 + 4g + j - 4 of the second
+// for j >= 4: the order in which lane group g holds its 8 probabilities.
+// `l` (0..127) picks one block and four consecutive positions. Rows at or
+// past `nvalid` get scale 1 (their p is 0, and a stale byte must not turn
+// 0 * V into NaN).
 __device__ __forceinline__ void format_scales(const uint8_t* buf, uint8_t* fmt, int delta,
-                                              int nvalid, int lane, int half) {
-  const int l = 64 * half + lane;
+                                              int nvalid, int l) {
   const int blk = l >> 3;
   const int pg = l & 7;
-  // positions 8g..8g+3: the 4 tokens of lane group g in the sub-tile of the
-  // half that reads this block (blk >> 3), 8g+4..8g+7: the other sub-tile's
-  const int row0 = 16 * ((pg & 1) ^ (blk >> 3)) + 4 * (pg >> 1);
+  const int row0 = 16 * (pg & 1) + 4 * (pg >> 1);
   const uint8_t* raw = buf + kLdsRaw + delta + blk;
   u32x4_t v;
   if (nvalid >= kTile) {
@@ -209,10 +209,20 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-struct WaveState {
-  f32x4_t o[16];     // O fragments of this half's 8 scale blocks: o[2b + parity]
-  f32x4_t l;         // softmax denominator of heads 4*grp + r (C layout, any column)
+// Running softmax statistics of the 16 heads, held by the wave that
+// computes the scores.
+struct SoftmaxState {
+  f32x4_t l;         // denominator of heads 4*grp + r (C layout, any column)
   float m;           // running max (base-2 scaled scores) of head `col`
+};
+
+// What the score wave hands the P V wave for one tile: P in the A-operand
+// layout of the bf16 MFMA (lane: head `col`, tokens of lane group `grp` in
+// the order of the formatted scales) and the factor that rescales O's rows
+// (heads 4*grp + r) before this tile is added (1 when the max is kept).
+struct TileHandoff {
+  u32x4_t p;
+  f32x4_t alpha;
 };
 
 // max(a, b, c) in one instruction (maxNum semantics, as fmaxf).
@@ -378,44 +388,35 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int delta, int
   return a0 + a1;
 }
 
-// Online-softmax update with the scores of the whole 32-token tile (s_own:
-// this wave's sub-tile `half`, s_oth: the partner's) and O += P V over this
-// half's scale blocks 8*half .. 8*half+7. Token tables are in "own sub-tile
-// first" order (x, p, the transposing reads, the formatted scales), so the
-// two waves of a pair hold the same (m, l) and P up to the order of tokens.
-__device__ __forceinline__ void softmax_pv(const uint8_t* buf, const uint8_t* fmt, int t0, int ke,
-                                           f32x4_t s_own, f32x4_t s_oth, WaveState& ws, float csc,
-                                           int lane, int half) {
-  const int col = lane & 15;
+// Online-softmax update with the scores of one 32-token tile (s0: tokens
+// 4*grp + r of the first sub-tile, s1: of the second, for head `col`):
+// returns the tile's hand-off to the P V wave and folds the bf16-rounded
+// P into l.
+__device__ __forceinline__ TileHandoff softmax_tile(f32x4_t s0, f32x4_t s1, int t0, int ke,
+                                                    SoftmaxState& st, float csc, int lane) {
   const int grp = lane >> 4;
-  const int own0 = 16 * half + 4 * grp;         // first own / other token of the lane group
-  const int oth0 = 16 * (1 - half) + 4 * grp;
-  float x[8] = {s_own[0], s_own[1], s_own[2], s_own[3], s_oth[0], s_oth[1], s_oth[2], s_oth[3]};
+  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
   if (t0 + kTile > ke) {   // tail tile: mask tokens past the item
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (t0 + own0 + r >= ke) x[r] = kNegInf;
-      if (t0 + oth0 + r >= ke) x[4 + r] = kNegInf;
+      if (t0 + 4 * grp + r >= ke) x[r] = kNegInf;
+      if (t0 + 16 + 4 * grp + r >= ke) x[4 + r] = kNegInf;
     }
   }
   float mx = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), fmaxf(x[6], x[7]));
   mx = max_over_groups(mx) * csc;
-  const bool need = mx > ws.m + kTau;
+  const bool need = mx > st.m + kTau;
+  TileHandoff h;
+  h.alpha = f32x4_t{1.f, 1.f, 1.f, 1.f};
   if (__ballot(need)) {
-    const float m_new = need ? mx : ws.m;
-    const float alpha = need ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;
-    ws.m = m_new;
-    float al[4];
+    const float m_new = need ? mx : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
+    st.m = m_new;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ws.l[r] *= al[r];
-#pragma unroll
-    for (int n = 0; n < 16; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ws.o[n][r] *= al[r];
+    for (int r = 0; r < 4; ++r) h.alpha[r] = __shfl(alpha, 4 * grp + r);
+    st.l *= h.alpha;
   }
-  const float base = ws.m;
+  const float base = st.m;
   float p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], csc, -base));
@@ -424,77 +425,89 @@ __device__ __forceinline__ void softmax_pv(const uint8_t* buf, const uint8_t* fm
   // l += sum_t P[h][t] of the same bf16-rounded P that multiplies V
   const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-  ws.l = mfma(pa, ones, ws.l);
+  st.l = mfma(pa, ones, st.l);
+  h.p = __builtin_bit_cast(u32x4_t, pa);
+  return h;
+}
 
+// One scale block (32 latent dims) of O += P V: decode the 8 tokens' V bytes
+// with their scales and multiply. LB is the block, the reads of block LB + 1
+// are issued before this block's wait so that they overlap its decode.
+template <int LB>
+__device__ __forceinline__ void pv_block(uint32_t tra, uint32_t sca, u32x2_t& v_cur, u32x4_t& s_lo,
+                                         u32x4_t& s_hi, const bf16x8_t (&az)[4], f32x4_t (&o)[32]) {
+  constexpr int kScStep = kTile * 4;
+  u32x2_t v_nx;
+  u32x4_t s_nlo, s_nhi;
+  if constexpr (LB + 1 < kVBlocks) {
+    v_nx = lds_tr8<16 * (LB + 1)>(tra);
+    s_nlo = lds_b128<(LB + 1) * kScStep>(sca);
+    s_nhi = lds_b128<(LB + 1) * kScStep + 16>(sca);
+    asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(v_cur), "+v"(s_lo), "+v"(s_hi));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v_cur), "+v"(s_lo), "+v"(s_hi));
+  }
+  const uint32_t sv[8] = {s_lo[0], s_lo[1], s_lo[2], s_lo[3], s_hi[0], s_hi[1], s_hi[2], s_hi[3]};
+  uint32_t c[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const float scl = __builtin_bit_cast(float, sv[kk]);
+    const uint32_t src = kk < 4 ? v_cur[0] : v_cur[1];
+    bf16x2_t cv;
+    switch (kk & 3) {
+      case 0: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0); break;
+      case 1: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1); break;
+      case 2: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2); break;
+      default: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3); break;
+    }
+    c[kk] = __builtin_bit_cast(uint32_t, cv);
+  }
+  const u32x4_t b1 = {c[0], c[1], c[2], c[3]};
+  const u32x4_t b2 = {c[4], c[5], c[6], c[7]};
+  const bf16x8_t vb1 = __builtin_bit_cast(bf16x8_t, b1), vb2 = __builtin_bit_cast(bf16x8_t, b2);
+  o[2 * LB] = mfma(az[2], vb2, mfma(az[0], vb1, o[2 * LB]));
+  o[2 * LB + 1] = mfma(az[3], vb2, mfma(az[1], vb1, o[2 * LB + 1]));
+  if constexpr (LB + 1 < kVBlocks) {
+    v_cur = v_nx;
+    s_lo = s_nlo;
+    s_hi = s_nhi;
+    pv_block<LB + 1>(tra, sca, v_cur, s_lo, s_hi, az, o);
+  }
+}
+
+// O += P V over all 512 latent dims for one tile (rows in `buf`, formatted
+// scales in `fmt`), after rescaling O by the hand-off's alpha.
+__device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, const TileHandoff& h,
+                                        f32x4_t (&o)[32], int lane) {
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const bool resc = h.alpha[0] != 1.f || h.alpha[1] != 1.f || h.alpha[2] != 1.f || h.alpha[3] != 1.f;
+  if (__ballot(resc)) {
+#pragma unroll
+    for (int n = 0; n < 32; ++n) o[n] *= h.alpha;
+  }
   // P V contracts over (token, dim parity) pairs: the decoded V dword of
   // token k holds (V[t_k][2j], V[t_k][2j+1]), so the B operand is the
   // decoder output as is, and P is spread into the even (resp. odd) K slots
-  // of the A operand with zeros in the others. pz[e + 2*g2] covers tokens
+  // of the A operand with zeros in the others. az[e + 2*g2] covers tokens
   // 4*g2 .. 4*g2+3 of the lane group for output parity e.
-  const u32x4_t pw = __builtin_bit_cast(u32x4_t, pa);
+  const u32x4_t pw = h.p;
   const u32x4_t pz0 = {pw[0] & 0xFFFFu, pw[0] >> 16, pw[1] & 0xFFFFu, pw[1] >> 16};
   const u32x4_t pz1 = {pw[0] << 16, pw[0] & 0xFFFF0000u, pw[1] << 16, pw[1] & 0xFFFF0000u};
   const u32x4_t pz2 = {pw[2] & 0xFFFFu, pw[2] >> 16, pw[3] & 0xFFFFu, pw[3] >> 16};
   const u32x4_t pz3 = {pw[2] << 16, pw[2] & 0xFFFF0000u, pw[3] << 16, pw[3] & 0xFFFF0000u};
-  const bf16x8_t a_e1 = __builtin_bit_cast(bf16x8_t, pz0), a_o1 = __builtin_bit_cast(bf16x8_t, pz1);
-  const bf16x8_t a_e2 = __builtin_bit_cast(bf16x8_t, pz2), a_o2 = __builtin_bit_cast(bf16x8_t, pz3);
-
+  const bf16x8_t az[4] = {__builtin_bit_cast(bf16x8_t, pz0), __builtin_bit_cast(bf16x8_t, pz1),
+                          __builtin_bit_cast(bf16x8_t, pz2), __builtin_bit_cast(bf16x8_t, pz3)};
   // lane (col, grp) supplies row k = col/2 of its group's 8 tokens, bytes
   // 8*(col&1).. of a 16-byte column block; it receives byte (16B + col) of
-  // all 8 tokens, in the same token order as p[0..7].
+  // all 8 tokens, in the order of the formatted scales.
   const int k = col >> 1;
-  const int trow = (k < 4) ? (own0 + k) : (oth0 + (k - 4));
-  const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1)) + 128 * half;
-  // the 8 tokens' formatted scales of block (8*half + lb): 32 bytes
-  const uint32_t sca = lds_addr(fmt + 32 * grp) + 8 * half * (kTile * 4);
-  // Per block: one transposing read and two scale reads; the next block's
-  // reads are in flight while this one is decoded.
+  const int trow = 4 * grp + (k & 3) + 16 * (k >> 2);
+  const uint32_t tra = lds_addr(buf + trow * kLdsRow + 8 * (col & 1));
+  const uint32_t sca = lds_addr(fmt + 32 * grp);
   u32x2_t v_cur = lds_tr8<0>(tra);
   u32x4_t s_lo = lds_b128<0>(sca), s_hi = lds_b128<16>(sca);
-#pragma unroll
-  for (int lb = 0; lb < 8; ++lb) {
-    u32x2_t v_nx;
-    u32x4_t s_nlo, s_nhi;
-    constexpr int kScStep = kTile * 4;
-    switch (lb) {
-      case 0: v_nx = lds_tr8<16>(tra); s_nlo = lds_b128<kScStep>(sca); s_nhi = lds_b128<kScStep + 16>(sca); break;
-      case 1: v_nx = lds_tr8<32>(tra); s_nlo = lds_b128<2 * kScStep>(sca); s_nhi = lds_b128<2 * kScStep + 16>(sca); break;
-      case 2: v_nx = lds_tr8<48>(tra); s_nlo = lds_b128<3 * kScStep>(sca); s_nhi = lds_b128<3 * kScStep + 16>(sca); break;
-      case 3: v_nx = lds_tr8<64>(tra); s_nlo = lds_b128<4 * kScStep>(sca); s_nhi = lds_b128<4 * kScStep + 16>(sca); break;
-      case 4: v_nx = lds_tr8<80>(tra); s_nlo = lds_b128<5 * kScStep>(sca); s_nhi = lds_b128<5 * kScStep + 16>(sca); break;
-      case 5: v_nx = lds_tr8<96>(tra); s_nlo = lds_b128<6 * kScStep>(sca); s_nhi = lds_b128<6 * kScStep + 16>(sca); break;
-      case 6: v_nx = lds_tr8<112>(tra); s_nlo = lds_b128<7 * kScStep>(sca); s_nhi = lds_b128<7 * kScStep + 16>(sca); break;
-      default: break;
-    }
-    if (lb < 7) {
-      asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(v_cur), "+v"(s_lo), "+v"(s_hi));
-    } else {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v_cur), "+v"(s_lo), "+v"(s_hi));
-    }
-    const uint32_t sv[8] = {s_lo[0], s_lo[1], s_lo[2], s_lo[3], s_hi[0], s_hi[1], s_hi[2], s_hi[3]};
-    uint32_t c[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const float scl = __builtin_bit_cast(float, sv[kk]);
-      const uint32_t src = kk < 4 ? v_cur[0] : v_cur[1];
-      bf16x2_t cv;
-      switch (kk & 3) {
-        case 0: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0); break;
-        case 1: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1); break;
-        case 2: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2); break;
-        default: cv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3); break;
-      }
-      c[kk] = __builtin_bit_cast(uint32_t, cv);
-    }
-    const u32x4_t b1 = {c[0], c[1], c[2], c[3]};
-    const u32x4_t b2 = {c[4], c[5], c[6], c[7]};
-    const bf16x8_t vb1 = __builtin_bit_cast(bf16x8_t, b1), vb2 = __builtin_bit_cast(bf16x8_t, b2);
-    ws.o[2 * lb] = mfma(a_e2, vb2, mfma(a_e1, vb1, ws.o[2 * lb]));
-    ws.o[2 * lb + 1] = mfma(a_o2, vb2, mfma(a_o1, vb1, ws.o[2 * lb + 1]));
-    if (lb < 7) {
-      v_cur = v_nx; s_lo = s_nlo; s_hi = s_nhi;
-    }
-  }
+  pv_block<0>(tra, sca, v_cur, s_lo, s_hi, az, o);
 }
 
 __global__ void __launch_bounds__(kThreads, 1)
@@ -506,7 +519,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & 3;
-  const int half = wave >> 2;
+  const bool scorer = (wave >> 2) != 0;   // else the pair's P V wave
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -515,11 +528,11 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int32_t* slot_indptr = plan + plan[kPwOffSlot];
   const int32_t* items = plan + plan[kPwOffItems];
   uint8_t* ring = lds + pair * kLdsPair;
-  f32x4_t* xchg = (f32x4_t*)(lds + kLdsXchg);
+  TileHandoff* hand = (TileHandoff*)(lds + kLdsXchg) + pair * 64 + lane;  // + parity * kPairs * 64
   uint8_t* fmt_pair = lds + kLdsFmt + pair * kFmtTile;  // + parity * kPairs * kFmtTile
-  // The two waves sharing a SIMD run the same instruction stream; giving
-  // one of them issue priority staggers them within a round.
-  if (half) __builtin_amdgcn_s_setprio(1);
+  // The scorer's results gate the next round of both waves: it gets issue
+  // priority over the P V wave on the shared SIMD.
+  if (scorer) __builtin_amdgcn_s_setprio(1);
 
   for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
     const int i_begin = slot_indptr[slot];
@@ -532,62 +545,73 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int ke = min(items[4 * it + 2], seq_hi);
       const int dest = items[4 * it + 3];
 
-      const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp);
-
-      WaveState ws;
-#pragma unroll
-      for (int n = 0; n < 16; ++n) ws.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      ws.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      ws.m = kMInit;
-
-      __syncthreads();  // LDS of the previous item's merge is free again
       const int len = ke - kb;
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
       const int t_first = kb + kTile * pair;
       const int ntiles = t_first < ke ? (ke - t_first + kTileStride - 1) / kTileStride : 0;
-      if (half && ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
-      // Round i: QK of tile i and P V of tile i-1 (whose scores the two
-      // halves swapped through LDS before this round's barrier). One tile is
-      // in flight while a round computes. Every wave runs all rounds (the
-      // barrier is workgroup-wide); a pair whose range is exhausted only syncs.
-      f32x4_t s_prev = {0.f, 0.f, 0.f, 0.f};
-      for (int i = 0; i <= rounds; ++i) {
-        const bool qk_on = i < ntiles;
-        const bool pv_on = i >= 1 && i - 1 < ntiles;
-        if (half && qk_on) wait_dma();
-        __syncthreads();  // tile i landed; tile i-2 fully consumed; scores of i-1 visible
-        if (half && i + 1 < ntiles) {
-          const int tn = t_first + (i + 1) * kTileStride;
-          stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, lane);
-        }
-        if (pv_on) {
-          const int tp = t_first + (i - 1) * kTileStride;
-          const f32x4_t s_other = xchg[(((i - 1) & 1) * kWaves + (wave ^ 4)) * 64 + lane];
-          softmax_pv(ring + ((i - 1) % kNumBuf) * kLdsBuf, fmt_pair + ((i - 1) & 1) * (kPairs * kFmtTile),
-                     tp, ke, s_prev, s_other, ws, csc, lane, half);
-        }
-        if (qk_on) {
-          const int tq = t_first + i * kTileStride;
-          const uint8_t* bq = ring + (i % kNumBuf) * kLdsBuf;
-          const int dq = raw_delta(sc, tq);
-          s_prev = qk_subtile(bq, dq, half, qo, lane);
-          // V scales of tile i for its P V in the next round
-          format_scales(bq, fmt_pair + (i & 1) * (kPairs * kFmtTile), dq, ke - tq, lane, half);
-          xchg[((i & 1) * kWaves + wave) * 64 + lane] = s_prev;
-        }
-      }
 
-      // ---- merge the 4 pairs' states (the two halves share m and l) ----
-      __syncthreads();
+      // The pair splits a tile's work by role, each wave on its own loop
+      // (both pass the same workgroup barriers, one per round):
+      //  * the scorer stages tiles (one in flight), computes S for the whole
+      //    tile, runs the softmax and formats the V scales;
+      //  * the P V wave accumulates O over all 512 dims one round later.
+      // Round i: scores of tile i, P V of tile i - 1.
+      // Each role's state lives only on its own path (it is written to LDS
+      // for the merge before the paths join).
       f32x4_t* frag = (f32x4_t*)lds;
       float* stats = (float*)(lds + kMergeFrag);
+      if (scorer) {
+        SoftmaxState st;
+        st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st.m = kMInit;
+        const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp);
+        __syncthreads();  // LDS of the previous item's merge is free again
+        if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
+        for (int i = 0; i <= rounds; ++i) {
+          const bool qk_on = i < ntiles;
+          if (qk_on) wait_dma();
+          __syncthreads();  // tile i landed; tile i-2 fully consumed; hand-off of i-1 visible
+          if (i + 1 < ntiles) {
+            const int tn = t_first + (i + 1) * kTileStride;
+            stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, lane);
+          }
+          if (qk_on) {
+            const int tq = t_first + i * kTileStride;
+            const uint8_t* bq = ring + (i % kNumBuf) * kLdsBuf;
+            const int dq = raw_delta(sc, tq);
+            const f32x4_t s0 = qk_subtile(bq, dq, 0, qo, lane);
+            const f32x4_t s1 = qk_subtile(bq, dq, 1, qo, lane);
+            hand[(i & 1) * (kPairs * 64)] = softmax_tile(s0, s1, tq, ke, st, csc, lane);
+            uint8_t* fm = fmt_pair + (i & 1) * (kPairs * kFmtTile);
+            format_scales(bq, fm, dq, ke - tq, lane);
+            format_scales(bq, fm, dq, ke - tq, 64 + lane);
+          }
+        }
+        __syncthreads();  // all rounds done: the ring area is free for the merge
+        if (grp == 0) stats[(2 * pair) * kHeads + col] = st.m;
+        if (col == 0) {
 #pragma unroll
-      for (int f = 0; f < 16; ++f) frag[(wave * 16 + f) * 64 + lane] = ws.o[f];
-      if (half == 0 && grp == 0) stats[(2 * pair) * kHeads + col] = ws.m;
-      if (half == 0 && col == 0) {
+          for (int r = 0; r < 4; ++r) stats[(2 * pair + 1) * kHeads + 4 * grp + r] = st.l[r];
+        }
+      } else {
+        f32x4_t o[32];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) stats[(2 * pair + 1) * kHeads + 4 * grp + r] = ws.l[r];
+        for (int n = 0; n < 32; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        for (int i = 0; i <= rounds; ++i) {
+          __syncthreads();
+          if (i >= 1 && i - 1 < ntiles) {
+            const TileHandoff h = hand[((i - 1) & 1) * (kPairs * 64)];
+            pv_tile(ring + ((i - 1) % kNumBuf) * kLdsBuf, fmt_pair + ((i - 1) & 1) * (kPairs * kFmtTile),
+                    h, o, lane);
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int f = 0; f < 32; ++f) frag[(pair * 32 + f) * 64 + lane] = o[f];
       }
+
+      // ---- merge the 4 pairs' states ----
       __syncthreads();
 
       float wgt[4][kPairs];
@@ -613,18 +637,15 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         inv[r] = lsum != 0.f ? 1.0f / lsum : 0.f;
         lse[r] = lsum != 0.f ? mmax + __builtin_amdgcn_logf(lsum) : kNegInf;
       }
-      // wave w handles scale blocks 2w, 2w+1 (both dim parities)
+      // wave w writes scale blocks 2w, 2w+1 (both dim parities)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const int blk = 2 * wave + bb;
-        const int hb = blk >> 3;      // half that accumulated this block
-        const int lb = blk & 7;
         f32x4_t ev = {0.f, 0.f, 0.f, 0.f}, od = ev;
 #pragma unroll
         for (int w = 0; w < kPairs; ++w) {
-          const int src_wave = w + 4 * hb;
-          const f32x4_t fe = frag[(src_wave * 16 + 2 * lb) * 64 + lane];
-          const f32x4_t fo = frag[(src_wave * 16 + 2 * lb + 1) * 64 + lane];
+          const f32x4_t fe = frag[(w * 32 + 2 * blk) * 64 + lane];
+          const f32x4_t fo = frag[(w * 32 + 2 * blk + 1) * 64 + lane];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             ev[r] += wgt[r][w] * fe[r];
