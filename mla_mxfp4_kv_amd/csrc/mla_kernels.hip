@@ -30,8 +30,10 @@
 //    more than 8), and the V scales rewritten as converter operands.
 //  * P V wave: O += P V for all 512 latent dims (O in 128 registers) on the
 //    bf16 MFMA. V comes from the packed LDS tile through ds_read_b64_tr_b8
-//    (8 tokens x 1 byte per lane), is decoded with each token's scale; the
-//    even and odd latent dims of a 32-dim scale block form two output tiles.
+//    (8 tokens x 1 byte per lane) and is decoded with each token's scale
+//    into (even dim, odd dim) pairs; v_perm_b32 regroups them into token
+//    pairs, so the even and odd latent dims of a 32-dim scale block are two
+//    output tiles with the whole tile's 32 tokens as K.
 //  * The 4 pairs' (m, l, O) are merged through LDS; a whole-sequence item
 //    writes bf16 output directly, any other item writes a normalised fp32
 //    partial and its base-2 LSE for the reduce kernel.
@@ -435,7 +437,7 @@ __device__ __forceinline__ TileHandoff softmax_tile(f32x4_t s0, f32x4_t s1, int 
 // are issued before this block's wait so that they overlap its decode.
 template <int LB>
 __device__ __forceinline__ void pv_block(uint32_t tra, uint32_t sca, u32x2_t& v_cur, u32x4_t& s_lo,
-                                         u32x4_t& s_hi, const bf16x8_t (&az)[4], f32x4_t (&o)[32]) {
+                                         u32x4_t& s_hi, const bf16x8_t& pa, f32x4_t (&o)[32]) {
   constexpr int kScStep = kTile * 4;
   u32x2_t v_nx;
   u32x4_t s_nlo, s_nhi;
@@ -462,16 +464,19 @@ __device__ __forceinline__ void pv_block(uint32_t tra, uint32_t sca, u32x2_t& v_
     }
     c[kk] = __builtin_bit_cast(uint32_t, cv);
   }
-  const u32x4_t b1 = {c[0], c[1], c[2], c[3]};
-  const u32x4_t b2 = {c[4], c[5], c[6], c[7]};
-  const bf16x8_t vb1 = __builtin_bit_cast(bf16x8_t, b1), vb2 = __builtin_bit_cast(bf16x8_t, b2);
-  o[2 * LB] = mfma(az[2], vb2, mfma(az[0], vb1, o[2 * LB]));
-  o[2 * LB + 1] = mfma(az[3], vb2, mfma(az[1], vb1, o[2 * LB + 1]));
+  // B operands of the block's even (odd) dims: the low (high) halves of the
+  // decoded dwords, two tokens per dword
+  const u32x4_t be = {__builtin_amdgcn_perm(c[1], c[0], 0x05040100u), __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
+                      __builtin_amdgcn_perm(c[5], c[4], 0x05040100u), __builtin_amdgcn_perm(c[7], c[6], 0x05040100u)};
+  const u32x4_t bo = {__builtin_amdgcn_perm(c[1], c[0], 0x07060302u), __builtin_amdgcn_perm(c[3], c[2], 0x07060302u),
+                      __builtin_amdgcn_perm(c[5], c[4], 0x07060302u), __builtin_amdgcn_perm(c[7], c[6], 0x07060302u)};
+  o[2 * LB] = mfma(pa, __builtin_bit_cast(bf16x8_t, be), o[2 * LB]);
+  o[2 * LB + 1] = mfma(pa, __builtin_bit_cast(bf16x8_t, bo), o[2 * LB + 1]);
   if constexpr (LB + 1 < kVBlocks) {
     v_cur = v_nx;
     s_lo = s_nlo;
     s_hi = s_nhi;
-    pv_block<LB + 1>(tra, sca, v_cur, s_lo, s_hi, az, o);
+    pv_block<LB + 1>(tra, sca, v_cur, s_lo, s_hi, pa, o);
   }
 }
 
@@ -486,18 +491,9 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
 #pragma unroll
     for (int n = 0; n < 32; ++n) o[n] *= h.alpha;
   }
-  // P V contracts over (token, dim parity) pairs: the decoded V dword of
-  // token k holds (V[t_k][2j], V[t_k][2j+1]), so the B operand is the
-  // decoder output as is, and P is spread into the even (resp. odd) K slots
-  // of the A operand with zeros in the others. az[e + 2*g2] covers tokens
-  // 4*g2 .. 4*g2+3 of the lane group for output parity e.
-  const u32x4_t pw = h.p;
-  const u32x4_t pz0 = {pw[0] & 0xFFFFu, pw[0] >> 16, pw[1] & 0xFFFFu, pw[1] >> 16};
-  const u32x4_t pz1 = {pw[0] << 16, pw[0] & 0xFFFF0000u, pw[1] << 16, pw[1] & 0xFFFF0000u};
-  const u32x4_t pz2 = {pw[2] & 0xFFFFu, pw[2] >> 16, pw[3] & 0xFFFFu, pw[3] >> 16};
-  const u32x4_t pz3 = {pw[2] << 16, pw[2] & 0xFFFF0000u, pw[3] << 16, pw[3] & 0xFFFF0000u};
-  const bf16x8_t az[4] = {__builtin_bit_cast(bf16x8_t, pz0), __builtin_bit_cast(bf16x8_t, pz1),
-                          __builtin_bit_cast(bf16x8_t, pz2), __builtin_bit_cast(bf16x8_t, pz3)};
+  // A operand: P of head `col` at the 8 tokens of lane group `grp`, in the
+  // order of the V rows below (K = the tile's 32 tokens).
+  const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, h.p);
   // lane (col, grp) supplies row k = col/2 of its group's 8 tokens, bytes
   // 8*(col&1).. of a 16-byte column block; it receives byte (16B + col) of
   // all 8 tokens, in the order of the formatted scales.
@@ -507,7 +503,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
   const uint32_t sca = lds_addr(fmt + 32 * grp);
   u32x2_t v_cur = lds_tr8<0>(tra);
   u32x4_t s_lo = lds_b128<0>(sca), s_hi = lds_b128<16>(sca);
-  pv_block<0>(tra, sca, v_cur, s_lo, s_hi, az, o);
+  pv_block<0>(tra, sca, v_cur, s_lo, s_hi, pa, o);
 }
 
 __global__ void __launch_bounds__(kThreads, 1)
