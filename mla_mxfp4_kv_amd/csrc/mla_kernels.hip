@@ -107,8 +107,10 @@ __device__ __forceinline__ int raw_delta(const uint8_t* sc, int t0) {
   return (int)((uintptr_t)(sc + (size_t)t0 * kBlocks) & 15);
 }
 
-// Issue the DMA of the tile starting at token t0 (`nvalid` = tokens of the
-// tile inside the item).
+// Issue DMA instructions kFirst .. kFirst + kCount - 1 of the tile starting
+// at token t0 (`nvalid` = tokens of the tile inside the item), and with
+// kScales the one for its scale rows.
+template <int kFirst, int kCount, bool kScales>
 __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
                                           const uint8_t* __restrict__ sc, int t0, int nvalid,
                                           int lane) {
@@ -120,21 +122,30 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
   const uint32_t lane_off = 16 * lane;
   if (nvalid >= kTile) {
 #pragma unroll
-    for (int i = 0; i < kRowDma; ++i)
+    for (int i = kFirst; i < kFirst + kCount; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(kv_t + 1024 * i + lane_off),
                                        (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
   } else {
     const uint32_t last = (uint32_t)(nvalid * kRowBytes - 16);
 #pragma unroll
-    for (int i = 0; i < kRowDma; ++i)
+    for (int i = kFirst; i < kFirst + kCount; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(kv_t + min(1024 * i + lane_off, last)),
                                        (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
   }
-  const uintptr_t first = (uintptr_t)(sc + (size_t)t0 * kBlocks);
-  const uintptr_t last_chunk = (first + (uintptr_t)(kBlocks * min(nvalid, kTile)) - 1) & ~(uintptr_t)15;
-  const uintptr_t src = min((first & ~(uintptr_t)15) + lane_off, last_chunk);
-  if (lane < kRawChunks)
-    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
+  if constexpr (kScales) {
+    const uintptr_t first = (uintptr_t)(sc + (size_t)t0 * kBlocks);
+    const uintptr_t last_chunk = (first + (uintptr_t)(kBlocks * min(nvalid, kTile)) - 1) & ~(uintptr_t)15;
+    const uintptr_t src = min((first & ~(uintptr_t)15) + lane_off, last_chunk);
+    if (lane < kRawChunks)
+      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
+  }
+}
+
+// The whole tile.
+__device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restrict__ kv,
+                                          const uint8_t* __restrict__ sc, int t0, int nvalid,
+                                          int lane) {
+  stage_dma<0, kRowDma, true>(buf, kv, sc, t0, nvalid, lane);
 }
 
 // Rewrite the V scales of a landed tile as exponent-field dwords (e << 23,
