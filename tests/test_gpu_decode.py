@@ -94,6 +94,34 @@ def test_small_cases_match_oracle(lens, num_cus):
     _check(got, want, f"lens={lens}")
 
 
+def test_cache_rows_before_the_first_sequence():
+    """kv_indptr[0] > 0: the rows before it belong to no sequence and are
+    never read as part of one (they hold NaN scales here)."""
+    lens = [40, 0, 300, 129]
+    _say(f"case lens={lens} base=77")
+    q, packed, scales, indptr, _ = _small(lens, seed=41)
+    base = 77
+    packed = torch.cat([torch.full((base, 288), 0x77, dtype=torch.uint8), packed])
+    scales = torch.cat([torch.full((base, 18), 255, dtype=torch.uint8), scales])
+    indptr = indptr + base
+    got = _run(q, packed, scales, indptr.tolist(), num_cus=3)
+    want = ref.mla_decode_ref(_qbits(q), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    assert not np.isnan(want).any()
+    _check(got, want, "base offset")
+
+
+def test_many_tiny_sequences_per_slot():
+    """Hundreds of 0..5-token sequences on 2 CUs: every slot walks a long
+    item list, each item a tail tile (and empties in between)."""
+    rng = np.random.default_rng(5)
+    lens = [int(v) for v in rng.integers(0, 6, size=400)]
+    _say(f"case 400 tiny sequences, {sum(lens)} tokens, num_cus=2")
+    q, packed, scales, indptr, _ = _small(lens, seed=43)
+    got = _run(q, packed, scales, indptr.tolist(), num_cus=2)
+    want = ref.mla_decode_ref(_qbits(q), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    _check(got, want, "tiny sequences")
+
+
 def test_token_scaled_and_wide_q():
     _say("case token-scaled KV, q std 2")
     q, packed, scales, indptr, _ = _small([900, 1500, 64], seed=11, q_std=2.0, token_scale=True)
