@@ -115,6 +115,30 @@ int mla_plan(const int32_t* kv_indptr_host, int32_t batch,
 int mla_plan_cus(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Build the work list on the GPU from a device copy of kv_indptr
+ * ([batch+1] int32, 4-byte aligned): one kernel enqueued on `stream`, no
+ * host synchronisation and no host read of the offsets, so plan + decode can
+ * be recorded in one HIP graph and replayed while kv_indptr changes in place
+ * (page "kernelbot-amd-mixed-mla-717900" records both decode stages in a
+ * graph; page "kernelbot-amd-mixed-mla-608791", host metadata builder, gives
+ * the work list this fills).
+ *
+ * Same plan rule and the same items, partial indices and reduce entries as
+ * mla_plan for the same offsets; only the section offsets differ, since the
+ * words are laid out for the bounds: every replay must keep
+ * kv_indptr[batch] - kv_indptr[0] <= max_total_kv, and the workspace must
+ * hold mla_workspace_bytes(batch, max_total_kv, num_cus) bytes.
+ * num_cus <= 0: the current device's count.
+ *
+ * Errors returned (nothing enqueued): MLA_ERR_INVALID (batch < 0,
+ * max_total_kv outside [0, 2^31), null or misaligned kv_indptr or
+ * workspace), MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP. Offsets that
+ * are invalid on the device (decreasing, kv_indptr[0] < 0, more than
+ * max_total_kv tokens) give an empty plan: header magic 0, no slots and no
+ * reduce entries, so the decode then writes nothing. */
+int mla_plan_device(const int32_t* kv_indptr_dev, int32_t batch, int64_t max_total_kv,
+                    int32_t num_cus, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-only planner: write the plan words for `num_cus` compute units into
  * `words` (host, `capacity_words` int32 entries). On success *num_words is
  * the word count and *workspace_bytes the workspace size the plan needs.
@@ -124,8 +148,8 @@ int mla_plan_host(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
                   int32_t* words, size_t capacity_words, size_t* num_words,
                   size_t* workspace_bytes);
 
-/* Run the decode planned into `workspace` by mla_plan (same kv_indptr
- * values). Enqueues the split-K decode kernel and, when some sequence is
+/* Run the decode planned into `workspace` by mla_plan or mla_plan_device
+ * (same kv_indptr values). Enqueues the split-K decode kernel and, when some sequence is
  * split or empty, the LSE-weighted reduce kernel on `stream`; never
  * synchronises. kv_indptr is the device copy of the offsets the plan was
  * built from; the kernels use it to bound every item to its sequence.

@@ -25,7 +25,7 @@ SCALES_PER_TOKEN = 18
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
     "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
-    "mla_plan", "mla_plan_cus", "mla_plan_host", "mla_decode_mxfp4",
+    "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
 )
 
 _lib = None
@@ -56,12 +56,14 @@ def lib():
     L.mla_plan.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.mla_plan_cus.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]
+    L.mla_plan_device.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.mla_plan_host.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_int32, c_i32p, ctypes.c_size_t,
                                 c_sizep, c_sizep]
     L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
-                 "mla_plan_host", "mla_decode_mxfp4"):
+                 "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -124,6 +126,16 @@ def plan(kv_indptr_host, workspace, num_cus: int = 0, stream=None):
            "mla_plan")
 
 
+def plan_device(kv_indptr_dev, batch: int, max_total_kv: int, workspace, num_cus: int = 0,
+                stream=None):
+    """Enqueue the GPU-side planner for the device tensor ``kv_indptr_dev``
+    (int32 [batch+1]) into ``workspace`` (no host synchronisation)."""
+    _check(lib().mla_plan_device(ctypes.c_void_p(kv_indptr_dev.data_ptr()), batch, max_total_kv,
+                                 num_cus, ctypes.c_void_p(workspace.data_ptr()),
+                                 workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "mla_plan_device")
+
+
 def decode(q, kv_packed, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
     """Enqueue the decode of a planned workspace on ``stream`` (no sync)."""
     _check(lib().mla_decode_mxfp4(
@@ -161,6 +173,37 @@ class MlaDecode:
         if kv_packed.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode(q, kv_packed, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+
+class MlaDecodeDevicePlan:
+    """Decode whose plan is built on the GPU from a device ``kv_indptr``
+    tensor, for any offsets of ``batch`` sequences with at most
+    ``max_total_kv`` tokens. ``plan(kv_indptr)`` and ``decode(...)`` only
+    enqueue kernels, so a sequence of them can be captured in a HIP graph.
+    """
+
+    def __init__(self, batch: int, max_total_kv: int, device="cuda", num_cus: int = 0):
+        import torch
+        self.batch = batch
+        self.max_total_kv = max_total_kv
+        self.num_cus = num_cus
+        self.device = torch.device(device)
+        nbytes = workspace_bytes(batch, max_total_kv, num_cus)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        assert self.workspace.data_ptr() % 256 == 0
+
+    def plan(self, kv_indptr, stream=None):
+        import torch
+        if kv_indptr.dtype != torch.int32 or tuple(kv_indptr.shape) != (self.batch + 1,) \
+                or not kv_indptr.is_contiguous() or kv_indptr.device.type != "cuda":
+            raise ValueError(f"kv_indptr must be a contiguous int32 device tensor [{self.batch + 1}]")
+        plan_device(kv_indptr, self.batch, self.max_total_kv, self.workspace, self.num_cus, stream)
+
+    def decode(self, q, kv_packed, kv_scale, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0),
+               stream=None):
+        _validate(q, kv_packed, kv_scale, out, self.batch)
+        decode(q, kv_packed, kv_scale, kv_indptr, out, sm_scale, self.workspace, stream)
         return out
 
 

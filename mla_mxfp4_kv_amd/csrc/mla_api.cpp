@@ -158,6 +158,41 @@ int mla_plan_cus(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, 
   return MLA_OK;
 }
 
+int mla_plan_device(const int32_t* kv_indptr_dev, int32_t batch, int64_t max_total_kv, int32_t num_cus,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int dev;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != MLA_OK) return st;
+  if (num_cus <= 0) num_cus = info.num_cus;
+  if (batch < 0) return fail(MLA_ERR_INVALID, "batch must be >= 0");
+  if (max_total_kv < 0 || max_total_kv > INT32_MAX)
+    return fail(MLA_ERR_INVALID, "max_total_kv must be in [0, 2^31)");
+  if (kv_indptr_dev == nullptr || !aligned(kv_indptr_dev, 4))
+    return fail(MLA_ERR_INVALID, "kv_indptr must be a non-null 4-byte aligned device pointer");
+  if (workspace == nullptr || !aligned(workspace, mla::kAlignBytes))
+    return fail(MLA_ERR_INVALID, "workspace must be a non-null 256-byte aligned device pointer");
+  const mla::DeviceLayout l = mla::device_layout(batch, max_total_kv, num_cus);
+  if (l.off_out > INT32_MAX) return fail(MLA_ERR_INVALID, "plan offsets exceed int32");
+  if ((size_t)l.total_bytes > workspace_bytes) {
+    char buf[160];
+    std::snprintf(buf, sizeof(buf), "workspace too small: the bounds need %lld bytes, got %zu",
+                  (long long)l.total_bytes, workspace_bytes);
+    return fail(MLA_ERR_WORKSPACE, buf);
+  }
+  hipError_t e = (hipError_t)mla::launch_plan_device(kv_indptr_dev, batch, num_cus, max_total_kv, l,
+                                                      workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_plan_kernel launch");
+  {
+    // the decode launches for the bounds; its kernels read the actual
+    // counts from the plan words
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_plans[(uintptr_t)workspace] = PlanEntry{dev, (int32_t)l.slots, batch, (int32_t)l.off_lse,
+                                              (int32_t)l.off_out, (size_t)l.total_bytes};
+  }
+  return MLA_OK;
+}
+
 int mla_plan(const int32_t* kv_indptr_host, int32_t batch, void* workspace, size_t workspace_bytes,
              void* stream) {
   return mla_plan_cus(kv_indptr_host, batch, 0, workspace, workspace_bytes, stream);

@@ -51,6 +51,15 @@ int build_plan(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
 // Upper bound on the workspace for any indptr of this size (mla_plan.cpp).
 size_t workspace_bound(int32_t batch, int64_t total, int32_t num_cus);
 
+// Plan layout sized for the bounds (batch sequences, at most max_total
+// tokens) rather than for one indptr: what the GPU-side planner fills
+// (mla_plan.cpp). Its total_bytes equals workspace_bound().
+struct DeviceLayout {
+  int64_t slots;        // bound on the slot count
+  int64_t off_items, off_reduce, off_lse, off_out, total_bytes;
+};
+DeviceLayout device_layout(int32_t batch, int64_t max_total, int32_t num_cus);
+
 // Kernel launchers (mla_kernels.hip). Return the hipError_t of the launch as int.
 struct DecodeArgs {
   const void* q;
@@ -66,6 +75,10 @@ struct DecodeArgs {
   int32_t num_reduce;
   int32_t grid;            // decode workgroups to launch
 };
+
+// GPU-side planner launch (mla_plan_kernel.hip).
+int launch_plan_device(const int32_t* kv_indptr, int32_t batch, int32_t num_cus, int64_t max_total,
+                       const DeviceLayout& l, void* workspace, void* stream);
 
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_reduce(const DecodeArgs& a, void* stream);

@@ -696,6 +696,8 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
   __shared__ f32x2_t acc_s[kReduceWaves][64];
   __shared__ float wsum_s[kReduceWaves];
   __shared__ float max_s[kReduceWaves];
+  // a plan built on the GPU is launched for its bound on the entry count
+  if ((int)blockIdx.x >= plan[kPwNumReduce]) return;
   const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
   const int b = ent[0];
   const int first = ent[1];

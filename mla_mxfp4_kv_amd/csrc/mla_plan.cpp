@@ -38,10 +38,19 @@ Layout layout_for(int64_t slots, int64_t items, int64_t reduce, int64_t partials
 
 }  // namespace
 
-size_t workspace_bound(int32_t batch, int64_t total, int32_t num_cus) {
+// A plan for at most `total` tokens has at most min(G, ceil(total /
+// MIN_CHUNK)) slots, one item per (slot, overlapping sequence) pair (so at
+// most slots + batch items), at most two partial items per slot (its first
+// and last) and at most one reduce entry per sequence.
+DeviceLayout device_layout(int32_t batch, int64_t max_total, int32_t num_cus) {
   const int64_t g = (int64_t)num_cus * MLA_PLAN_WG_PER_CU;
-  const int64_t slots = total <= 0 ? 0 : std::min<int64_t>(g, ceil_div(total, MLA_PLAN_MIN_CHUNK));
-  return (size_t)layout_for(slots, slots + batch, batch, 2 * slots).total_bytes;
+  const int64_t slots = max_total <= 0 ? 0 : std::min<int64_t>(g, ceil_div(max_total, MLA_PLAN_MIN_CHUNK));
+  const Layout l = layout_for(slots, slots + batch, batch, 2 * slots);
+  return DeviceLayout{slots, l.off_items, l.off_reduce, l.off_lse, l.off_out, l.total_bytes};
+}
+
+size_t workspace_bound(int32_t batch, int64_t total, int32_t num_cus) {
+  return (size_t)device_layout(batch, total, num_cus).total_bytes;
 }
 
 int build_plan(const int32_t* ind, int32_t batch, int32_t num_cus, PlanResult* out,
