@@ -16,6 +16,12 @@ Recipe (one generator, draws in a fixed order: lengths, Q, KV):
 
 The rows are generated in fixed-size chunks so that a given (seed, device)
 always yields the same bytes whatever the total size.
+
+The fp8 and bf16 sibling caches (:func:`make_dense_inputs`) take the same
+draws: the bf16 latent rows as they are, or those rows encoded as OCP E4M3
+with one per-tensor float32 scale ``amax / 448``, each value divided by it,
+clamped to +-448 and rounded to nearest even (the per-tensor recipe page
+"kernelbot-amd-mixed-mla-676098" applies to q in ``_aiter_mla_decode``).
 """
 
 from __future__ import annotations
@@ -99,12 +105,9 @@ def seq_lengths(w: Workload) -> list:
     return [int(v) for v in torch.randint(lo, hi + 1, (w.batch,), generator=g)]
 
 
-def make_inputs(w: Workload, device="cpu", lengths=None):
-    """Build (q bf16 [B,16,576], packed u8 [T,288], scales u8 [T,18],
-    kv_indptr int32 [B+1] on the host, lengths list) on ``device``.
-
-    ``lengths`` overrides the workload's length rule (for small test cases).
-    """
+def _draw(w: Workload, device, lengths):
+    """Lengths, bf16 Q and a generator of (row0, row1, bf16 latent rows)
+    chunks, in the fixed draw order."""
     device = torch.device(device)
     lens = seq_lengths(w) if lengths is None else [int(v) for v in lengths]
     batch = len(lens)
@@ -115,22 +118,79 @@ def make_inputs(w: Workload, device="cpu", lengths=None):
     g = torch.Generator(device=device).manual_seed(w.seed + 1000)
     q = (torch.randn(batch, NUM_HEADS, QK_DIM, generator=g, device=device,
                      dtype=torch.float32) * w.q_std).to(torch.bfloat16)
-    packed = torch.empty(total, PACKED_BYTES, dtype=torch.uint8, device=device)
-    scales = torch.empty(total, SCALES_PER_TOKEN, dtype=torch.uint8, device=device)
-    for r0 in range(0, total, _ROW_CHUNK):
-        r1 = min(total, r0 + _ROW_CHUNK)
-        x = torch.randn(r1 - r0, QK_DIM, generator=g, device=device, dtype=torch.float32)
-        if w.token_scale:
-            u = torch.rand(r1 - r0, 1, generator=g, device=device, dtype=torch.float32)
-            x = x * torch.exp2(4.0 * u - 2.0)
-        x = x.to(torch.bfloat16)
+
+    def rows():
+        for r0 in range(0, total, _ROW_CHUNK):
+            r1 = min(total, r0 + _ROW_CHUNK)
+            x = torch.randn(r1 - r0, QK_DIM, generator=g, device=device, dtype=torch.float32)
+            if w.token_scale:
+                u = torch.rand(r1 - r0, 1, generator=g, device=device, dtype=torch.float32)
+                x = x * torch.exp2(4.0 * u - 2.0)
+            yield r0, r1, x.to(torch.bfloat16)
+
+    return lens, torch.tensor(indptr, dtype=torch.int32), total, q, rows()
+
+
+def make_inputs(w: Workload, device="cpu", lengths=None):
+    """Build (q bf16 [B,16,576], packed u8 [T,288], scales u8 [T,18],
+    kv_indptr int32 [B+1] on the host, lengths list) on ``device``.
+
+    ``lengths`` overrides the workload's length rule (for small test cases).
+    """
+    lens, kv_indptr, total, q, rows = _draw(w, device, lengths)
+    packed = torch.empty(total, PACKED_BYTES, dtype=torch.uint8, device=q.device)
+    scales = torch.empty(total, SCALES_PER_TOKEN, dtype=torch.uint8, device=q.device)
+    for r0, r1, x in rows:
         pk, sc = quantize_mxfp4(x)
         packed[r0:r1] = pk
         scales[r0:r1] = sc
-    kv_indptr = torch.tensor(indptr, dtype=torch.int32)
     return q, packed, scales, kv_indptr, lens
 
 
-def kv_bytes(total_tokens: int) -> int:
-    """Algorithmic KV-cache bytes a decode call must read (packed + scales)."""
-    return total_tokens * (PACKED_BYTES + SCALES_PER_TOKEN)
+FP8_MAX = 448.0
+
+
+def quantize_fp8_per_tensor(x: torch.Tensor):
+    """OCP E4M3 codes (uint8, same shape) of ``x`` and the per-tensor float32
+    scale (a 1-element tensor): scale = amax / 448 (1 for an all-zero
+    tensor), codes = e4m3(clamp(x / scale, -448, 448)) rounded to nearest
+    even."""
+    amax = x.abs().amax().to(torch.float32) if x.numel() else torch.zeros((), device=x.device)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).reshape(1)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    flat = x.reshape(-1, x.shape[-1]) if x.dim() > 1 else x.reshape(1, -1)
+    out = codes.view(flat.shape)
+    for r0 in range(0, flat.shape[0], _ROW_CHUNK):
+        y = (flat[r0:r0 + _ROW_CHUNK].to(torch.float32) / scale).clamp(-FP8_MAX, FP8_MAX)
+        out[r0:r0 + _ROW_CHUNK] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def make_dense_inputs(w: Workload, fmt: str, device="cpu", lengths=None):
+    """The sibling caches of a workload, from the same draws as
+    :func:`make_inputs`: returns (q bf16 [B,16,576], cache, kv_scale,
+    kv_indptr int32 [B+1] on the host, lengths) with
+    * fmt "bf16": cache = the bf16 latent rows [T, 576], kv_scale None;
+    * fmt "fp8": cache = uint8 E4M3 codes [T, 576], kv_scale float32 [1].
+    """
+    if fmt not in ("bf16", "fp8"):
+        raise ValueError(f"unknown cache format {fmt!r}")
+    lens, kv_indptr, total, q, rows = _draw(w, device, lengths)
+    lat = torch.empty(total, QK_DIM, dtype=torch.bfloat16, device=q.device)
+    for r0, r1, x in rows:
+        lat[r0:r1] = x
+    if fmt == "bf16":
+        return q, lat, None, kv_indptr, lens
+    codes, scale = quantize_fp8_per_tensor(lat)
+    del lat
+    return q, codes, scale, kv_indptr, lens
+
+
+KV_BYTES_PER_TOKEN = {"mxfp4": PACKED_BYTES + SCALES_PER_TOKEN, "fp8": QK_DIM, "bf16": 2 * QK_DIM}
+
+
+def kv_bytes(total_tokens: int, fmt: str = "mxfp4") -> int:
+    """Algorithmic KV-cache bytes a decode call must read: packed rows +
+    E8M0 scales (mxfp4, 306 B/token), fp8 rows (576 B/token; the one
+    per-tensor scale is negligible) or bf16 rows (1152 B/token)."""
+    return total_tokens * KV_BYTES_PER_TOKEN[fmt]

@@ -21,7 +21,12 @@ Sources (kernelindex.com "amd-mixed-mla" leaderboard submission pages):
 Modules:
 
 * :mod:`oracle.mxfp4_ref` -- exact MXFP4 dequantisation and fp64 attention.
+* :mod:`oracle.dense_ref` -- exact fp8 (e4m3 + per-tensor scale) and bf16
+  cache decoding and the same fp64 attention, for the sibling decodes.
 * :mod:`oracle.planner_ref` -- the CPU reference work-list planner.
+
+Page "kernelbot-amd-mixed-mla-676098" also gives the fp8 cache (``_aiter_mla_decode``:
+fp8 rows + one per-tensor scale) and the bf16 cache (``_naive_fallback``).
 """
 
 from .mxfp4_ref import (  # noqa: F401
@@ -38,5 +43,17 @@ from .mxfp4_ref import (  # noqa: F401
     dequant_mxfp4,
     mla_decode_ref,
     mla_decode_ref_seq,
+)
+from .dense_ref import (  # noqa: F401
+    E4M3_VALUES,
+    FP8_MAX,
+    e4m3_value,
+    dequant_fp8,
+    dequant_bf16,
+    attention_f64,
+    mla_decode_ref_fp8,
+    mla_decode_ref_fp8_seq,
+    mla_decode_ref_bf16,
+    mla_decode_ref_bf16_seq,
 )
 from .planner_ref import plan_words_ref, PlanRef, decode_plan_words  # noqa: F401
