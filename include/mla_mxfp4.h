@@ -1,6 +1,7 @@
 /*
  * mla_mxfp4.h -- C ABI of libmla_mxfp4.so: MXFP4-KV absorbed-MLA decode for
- * AMD Instinct MI355X (gfx950).
+ * AMD Instinct MI355X (gfx950), with fp8-KV and bf16-KV sibling decodes on
+ * the same plan (mla_decode_fp8, mla_decode_bf16).
  *
  * The operation (kernelindex.com "amd-mixed-mla" submission pages):
  *   For each sequence b (one query token) and head h in 0..15,
@@ -153,15 +154,38 @@ int mla_plan_host(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
  * split or empty, the LSE-weighted reduce kernel on `stream`; never
  * synchronises. kv_indptr is the device copy of the offsets the plan was
  * built from; the kernels use it to bound every item to its sequence.
- * sm_scale is the softmax scale (1/sqrt(576) for this model).
+ * sm_scale is the softmax scale (1/sqrt(576) for this model); it must be
+ * finite and non-negative.
  *
  * Errors (nothing is enqueued): MLA_ERR_NOT_PLANNED, MLA_ERR_INVALID (null
- * or misaligned pointer, non-finite sm_scale), MLA_ERR_DEVICE, MLA_ERR_HIP
- * (launch failure). Faults inside the kernels surface as HIP errors on the
- * stream. */
+ * or misaligned pointer, non-finite or negative sm_scale), MLA_ERR_DEVICE,
+ * MLA_ERR_HIP (launch failure). Faults inside the kernels surface as HIP
+ * errors on the stream. */
 int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                      const int32_t* kv_indptr, void* out, float sm_scale,
                      void* workspace, void* stream);
+
+/* The same decode over an fp8 KV cache: kv_fp8 is uint8 [T, 576] (device,
+ * 16-byte aligned), each byte an OCP FP8 E4M3 code (the MI355X fp8 type:
+ * 4 exponent bits with bias 7, 3 mantissa bits, largest finite value 448,
+ * codes 0x7F/0xFF NaN), and kv_scale points to ONE float32 on the device
+ * (4-byte aligned) that scales the whole tensor: K[t,j] = e4m3(kv_fp8[t,j]) *
+ * kv_scale[0], V[t,:] = K[t,0:512]. This is the fp8 cache of page
+ * "kernelbot-amd-mixed-mla-676098" (_aiter_mla_decode: kv_fp8, kv_scale =
+ * kv_data["fp8"]). q, kv_indptr, out, sm_scale, the workspace (planned by
+ * mla_plan / mla_plan_device: the plan does not depend on the cache
+ * format), the stream, ownership and the error codes are those of
+ * mla_decode_mxfp4. */
+int mla_decode_fp8(const void* q, const void* kv_fp8, const float* kv_scale,
+                   const int32_t* kv_indptr, void* out, float sm_scale,
+                   void* workspace, void* stream);
+
+/* The same decode over a bf16 KV cache: kv_bf16 is bfloat16 [T, 576]
+ * (device, 16-byte aligned), K[t,:] = row t, V[t,:] = K[t,0:512] (page
+ * "kernelbot-amd-mixed-mla-676098", _naive_fallback reads kv_data["bf16"]).
+ * Everything else as for mla_decode_mxfp4. */
+int mla_decode_bf16(const void* q, const void* kv_bf16, const int32_t* kv_indptr,
+                    void* out, float sm_scale, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ SCALES_PER_TOKEN = 18
 EXPORTS = (
     "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
     "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
+    "mla_decode_fp8", "mla_decode_bf16",
 )
 
 _lib = None
@@ -62,8 +63,13 @@ def lib():
                                 c_sizep, c_sizep]
     L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
-                 "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4"):
+                 "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
+                 "mla_decode_bf16"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -145,6 +151,24 @@ def decode(q, kv_packed, kv_scale, kv_indptr_dev, out, sm_scale: float, workspac
         ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_mxfp4")
 
 
+def decode_fp8(q, kv_fp8, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
+    """Enqueue the fp8-cache decode (``kv_scale``: float32 [1] device tensor)."""
+    _check(lib().mla_decode_fp8(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_fp8.data_ptr()),
+        ctypes.c_void_p(kv_scale.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale),
+        ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_fp8")
+
+
+def decode_bf16(q, kv_bf16, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
+    """Enqueue the bf16-cache decode."""
+    _check(lib().mla_decode_bf16(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_bf16.data_ptr()),
+        ctypes.c_void_p(kv_indptr_dev.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)),
+        "mla_decode_bf16")
+
+
 class MlaDecode:
     """Holds a planned workspace for one kv_indptr and runs decode calls.
 
@@ -173,6 +197,40 @@ class MlaDecode:
         if kv_packed.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode(q, kv_packed, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+    def _out(self, q, out):
+        import torch
+        if out is None:
+            out = torch.empty(self.batch, NUM_HEADS, V_DIM, dtype=torch.bfloat16, device=self.device)
+        _validate_qo(q, out, self.batch)
+        return out
+
+    def fp8(self, q, kv_fp8, kv_scale, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        """Decode over an fp8 cache: kv_fp8 uint8 E4M3 codes [T,576], kv_scale
+        float32 [1] (per-tensor scale), both on the device."""
+        import torch
+        out = self._out(q, out)
+        if kv_fp8.dtype not in (torch.uint8, torch.float8_e4m3fn) or kv_fp8.dim() != 2 \
+                or kv_fp8.shape[1] != QK_DIM or not kv_fp8.is_contiguous():
+            raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [T,576]")
+        if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != kv_fp8.device:
+            raise ValueError("kv_scale must be a float32 device tensor of one element")
+        if kv_fp8.shape[0] < self.indptr_host[-1]:
+            raise ValueError("kv_indptr reaches past the end of the cache rows")
+        decode_fp8(q, kv_fp8, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+    def bf16(self, q, kv_bf16, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        """Decode over a bf16 cache: kv_bf16 bfloat16 [T,576] on the device."""
+        import torch
+        out = self._out(q, out)
+        if kv_bf16.dtype != torch.bfloat16 or kv_bf16.dim() != 2 or kv_bf16.shape[1] != QK_DIM \
+                or not kv_bf16.is_contiguous():
+            raise ValueError("kv_bf16 must be contiguous bfloat16 [T,576]")
+        if kv_bf16.shape[0] < self.indptr_host[-1]:
+            raise ValueError("kv_indptr reaches past the end of the cache rows")
+        decode_bf16(q, kv_bf16, self.kv_indptr, out, sm_scale, self.workspace, stream)
         return out
 
 
@@ -205,6 +263,14 @@ class MlaDecodeDevicePlan:
         _validate(q, kv_packed, kv_scale, out, self.batch)
         decode(q, kv_packed, kv_scale, kv_indptr, out, sm_scale, self.workspace, stream)
         return out
+
+
+def _validate_qo(q, out, batch):
+    import torch
+    if q.dtype != torch.bfloat16 or tuple(q.shape) != (batch, NUM_HEADS, QK_DIM) or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous bf16 [{batch},16,576], got {q.dtype} {tuple(q.shape)}")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (batch, NUM_HEADS, V_DIM) or not out.is_contiguous():
+        raise ValueError("out must be contiguous bf16 [B,16,512]")
 
 
 def _validate(q, kv_packed, kv_scale, out, batch):

@@ -63,7 +63,7 @@ int current_device(int* dev, DeviceInfo* info) {
   }
   *info = d;
   if (!d.is_gfx950) return fail(MLA_ERR_DEVICE, "the current HIP device is not gfx950 (MI355X)");
-  if (d.lds_per_block < mla::decode_lds_bytes())
+  if (d.lds_per_block < mla::decode_lds_bytes() || d.lds_per_block < mla::decode_dense_lds_bytes())
     return fail(MLA_ERR_DEVICE, "device LDS per workgroup is smaller than the decode kernel needs");
   return MLA_OK;
 }
@@ -198,9 +198,16 @@ int mla_plan(const int32_t* kv_indptr_host, int32_t batch, void* workspace, size
   return mla_plan_cus(kv_indptr_host, batch, 0, workspace, workspace_bytes, stream);
 }
 
-int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
-                     const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum class KvFormat { kMxfp4, kFp8, kBf16 };
+
+// Shared validation and launch of the three cache formats: the plan, the
+// partial layout and the reduce kernel are the same for all of them.
+int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_scale,
+                  const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
   int dev;
   DeviceInfo info;
   int st = current_device(&dev, &info);
@@ -214,7 +221,8 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
     pe = it->second;
   }
   if (pe.device != dev) return fail(MLA_ERR_INVALID, "workspace was planned on another device");
-  if (!std::isfinite(sm_scale)) return fail(MLA_ERR_INVALID, "sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || sm_scale < 0.0f)
+    return fail(MLA_ERR_INVALID, "sm_scale must be finite and non-negative");
   const bool any_work = pe.num_slots > 0 || pe.num_reduce > 0;
   if (any_work) {
     if (out == nullptr || !aligned(out, 16)) return fail(MLA_ERR_INVALID, "out must be non-null and 16-byte aligned");
@@ -222,13 +230,16 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
   }
   if (pe.num_slots > 0) {
     if (q == nullptr || !aligned(q, 16)) return fail(MLA_ERR_INVALID, "q must be non-null and 16-byte aligned");
-    if (kv_packed == nullptr || !aligned(kv_packed, 16))
-      return fail(MLA_ERR_INVALID, "kv_packed must be non-null and 16-byte aligned");
-    if (kv_scale == nullptr) return fail(MLA_ERR_INVALID, "kv_scale must be non-null");
+    const char* kv_name = fmt == KvFormat::kMxfp4 ? "kv_packed" : fmt == KvFormat::kFp8 ? "kv_fp8" : "kv_bf16";
+    if (kv == nullptr || !aligned(kv, 16))
+      return fail(MLA_ERR_INVALID, std::string(kv_name) + " must be non-null and 16-byte aligned");
+    if (fmt == KvFormat::kMxfp4 && kv_scale == nullptr) return fail(MLA_ERR_INVALID, "kv_scale must be non-null");
+    if (fmt == KvFormat::kFp8 && (kv_scale == nullptr || !aligned(kv_scale, 4)))
+      return fail(MLA_ERR_INVALID, "kv_scale must be a non-null 4-byte aligned device pointer");
   }
   mla::DecodeArgs a;
   a.q = q;
-  a.kv_packed = (const uint8_t*)kv_packed;
+  a.kv_packed = (const uint8_t*)kv;
   a.kv_scale = (const uint8_t*)kv_scale;
   a.kv_indptr = kv_indptr;
   a.out = out;
@@ -240,11 +251,38 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
   a.num_reduce = pe.num_reduce;
   const int gmax = info.num_cus * MLA_PLAN_WG_PER_CU;
   a.grid = pe.num_slots < gmax ? pe.num_slots : gmax;
-  hipError_t e = (hipError_t)mla::launch_decode(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_kernel launch");
+  hipError_t e;
+  if (fmt == KvFormat::kMxfp4) {
+    e = (hipError_t)mla::launch_decode(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "mla_decode_kernel launch");
+  } else {
+    e = (hipError_t)mla::launch_decode_dense(a, fmt == KvFormat::kFp8, (const float*)kv_scale, stream);
+    if (e != hipSuccess) return hip_fail(e, "mla_decode_dense_kernel launch");
+  }
   e = (hipError_t)mla::launch_reduce(a, stream);
   if (e != hipSuccess) return hip_fail(e, "mla_reduce_kernel launch");
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
+                     const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
+                     void* stream) {
+  return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, kv_indptr, out, sm_scale, workspace,
+                       stream);
+}
+
+int mla_decode_fp8(const void* q, const void* kv_fp8, const float* kv_scale, const int32_t* kv_indptr,
+                   void* out, float sm_scale, void* workspace, void* stream) {
+  return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, kv_indptr, out, sm_scale, workspace, stream);
+}
+
+int mla_decode_bf16(const void* q, const void* kv_bf16, const int32_t* kv_indptr, void* out,
+                    float sm_scale, void* workspace, void* stream) {
+  return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, kv_indptr, out, sm_scale, workspace, stream);
 }
 
 }  // extern "C"

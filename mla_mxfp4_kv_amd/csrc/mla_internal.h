@@ -83,7 +83,13 @@ int launch_plan_device(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_reduce(const DecodeArgs& a, void* stream);
 
-// Dynamic LDS bytes the decode kernel needs (for validation against the device).
+// fp8 / bf16 cache decode (mla_dense_kernels.hip): the same plan, partials
+// and reduce; a.kv_packed holds the cache rows, kv_scale the device pointer
+// of the fp8 per-tensor scale (unused for bf16).
+int launch_decode_dense(const DecodeArgs& a, bool fp8, const float* kv_scale, void* stream);
+
+// Static LDS bytes the decode kernels need (for validation against the device).
 size_t decode_lds_bytes();
+size_t decode_dense_lds_bytes();
 
 }  // namespace mla
