@@ -25,19 +25,29 @@ from mla_mxfp4_kv_amd import binding, synth
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_kernels.hip")
+KERNEL_SRC = {
+    "mxfp4": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_kernels.hip"),
+    "fp8": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
+    "bf16": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
+}
+KERNEL_NAME = {"mxfp4": "mla_decode_kernel", "fp8": "mla_decode_dense_kernel<true>",
+               "bf16": "mla_decode_dense_kernel<false>"}
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(fmt: str = "mxfp4") -> str:
+    with open(KERNEL_SRC[fmt], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def _profile_name(workload: str, fmt: str) -> str:
+    return f"decode_{workload}" if fmt == "mxfp4" else f"decode_{fmt}_{workload}"
+
+
+def measured_traffic(workload: str, fmt: str = "mxfp4"):
     """HBM bytes per decode launch from the committed rocprofv3 counter
     summary of this workload, if it was taken on the current kernel source
     (else None)."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{_profile_name(workload, fmt)}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -46,7 +56,7 @@ def measured_traffic(workload: str):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(fmt):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -69,20 +79,20 @@ QO_BYTES_PER_SEQ = 16 * 576 * 2 + 16 * 512 * 2
 PARTIAL_BYTES = 16 * (512 + 1) * 4
 
 
-def algorithmic_bytes(words, total_tokens):
-    """Bytes the decode must move: KV + scales, Q, output, and each split
+def algorithmic_bytes(words, total_tokens, fmt="mxfp4"):
+    """Bytes the decode must move: KV (+ scales), Q, output, and each split
     partial written once and read once."""
     num_partials = words[9]
     batch = words[2]
-    return (synth.kv_bytes(total_tokens) + batch * QO_BYTES_PER_SEQ
+    return (synth.kv_bytes(total_tokens, fmt) + batch * QO_BYTES_PER_SEQ
             + 2 * num_partials * PARTIAL_BYTES)
 
 
-def cpu_baseline(w, q, packed, scales, lens, budget_s):
+def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=None):
     """Time the fp64 oracle (as it stands) on whole sequences of the same
     workload until about ``budget_s`` seconds of CPU work."""
     import numpy as np
-    from oracle import mxfp4_ref
+    from oracle import dense_ref, mxfp4_ref
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -97,22 +107,31 @@ def cpu_baseline(w, q, packed, scales, lens, budget_s):
     oracle_s = 0.0
     for b in range(len(lens)):
         lo, hi = ind[b], ind[b + 1]
-        pk = packed[lo:hi].cpu().numpy()
-        sc = scales[lo:hi].cpu().numpy()
-        t0 = time.perf_counter()          # device->host copies are not timed
-        mxfp4_ref.mla_decode_ref_seq(qb[b], pk, sc, w.sm_scale)
+        if fmt == "mxfp4":
+            pk = packed[lo:hi].cpu().numpy()
+            sc = scales[lo:hi].cpu().numpy()
+            t0 = time.perf_counter()          # device->host copies are not timed
+            mxfp4_ref.mla_decode_ref_seq(qb[b], pk, sc, w.sm_scale)
+        elif fmt == "fp8":
+            rows = packed[lo:hi].cpu().numpy()
+            t0 = time.perf_counter()
+            dense_ref.mla_decode_ref_fp8_seq(qb[b], rows, kv_scale, w.sm_scale)
+        else:
+            rows = packed[lo:hi].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            dense_ref.mla_decode_ref_bf16_seq(qb[b], rows, w.sm_scale)
         oracle_s += time.perf_counter() - t0
         done_tokens += hi - lo
         n_seq += 1
         if oracle_s >= budget_s:
             break
-    gbs = synth.kv_bytes(done_tokens) / oracle_s / 1e9
+    gbs = synth.kv_bytes(done_tokens, fmt) / oracle_s / 1e9
     return {
         "value": round(gbs, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"first {n_seq} of {len(lens)} sequences ({done_tokens} tokens) of {w.name}, "
+        "sample": f"first {n_seq} of {len(lens)} sequences ({done_tokens} tokens) of {w.name} ({fmt} cache), "
                   f"{oracle_s:.1f} s, us/call extrapolated "
                   f"{oracle_s / done_tokens * sum(lens) * 1e6:.0f}",
     }
@@ -124,6 +143,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="b256_kv8192", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--kv-format", default="mxfp4", choices=["mxfp4", "fp8", "bf16"],
+                    help="cache format: the MXFP4 headline path, or the fp8 / bf16 sibling decodes")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
@@ -146,19 +167,35 @@ def main(argv=None):
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
-    q, packed, scales, indptr, lens = synth.make_inputs(w, device=dev)
+    fmt = args.kv_format
+    print(f"[bench] generating {w.name} ({fmt} cache)", file=sys.stderr, flush=True)
+    if fmt == "mxfp4":
+        q, packed, scales, indptr, lens = synth.make_inputs(w, device=dev)
+        kv_scale_host = None
+    else:
+        # `packed` holds the cache rows, `scales` the fp8 per-tensor scale
+        q, packed, scales, indptr, lens = synth.make_dense_inputs(w, fmt, device=dev)
+        kv_scale_host = float(scales[0]) if fmt == "fp8" else None
     total = int(indptr[-1])
     t_plan = time.perf_counter()
     dec = binding.MlaDecode(indptr.tolist(), device=dev)
     plan_ms = (time.perf_counter() - t_plan) * 1e3
     words, _ = binding.plan_host(indptr.tolist(), binding.num_cus())
     out = torch.empty(w.batch, 16, 512, dtype=torch.bfloat16, device=dev)
+    if fmt == "mxfp4":
+        def call():
+            dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+    elif fmt == "fp8":
+        def call():
+            dec.fp8(q, packed, scales, out=out, sm_scale=w.sm_scale)
+    else:
+        def call():
+            dec.bf16(q, packed, out=out, sm_scale=w.sm_scale)
     flush = torch.ones(1 << 27, dtype=torch.int64, device=dev) if args.cold else None
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+        call()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -171,7 +208,7 @@ def main(argv=None):
         ev_b = torch.cuda.Event(enable_timing=True)
         ev_a.record(stream)
         for _ in range(args.steps):
-            dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+            call()
         ev_b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
@@ -183,7 +220,7 @@ def main(argv=None):
         for i in range(args.steps):
             flush.sum()
             ev0[i].record(stream)
-            dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+            call()
             ev1[i].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
@@ -196,27 +233,28 @@ def main(argv=None):
         if flush is not None:
             flush.sum()
         ev0[i].record(stream)
-        dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+        call()
         ev1[i].record(stream)
     torch.cuda.synchronize()
     call_us = [a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)]
     med_us = statistics.median(call_us)
     ms_per_step = wall / args.steps * 1e3
-    kvb = synth.kv_bytes(total)
+    kvb = synth.kv_bytes(total, fmt)
     # whole-job throughput (wall clock over the timed steps); with --cold the
     # wall clock includes the flushes, so the event time is used instead
     step_s = (avg_us * 1e-6) if args.cold else (wall / args.steps)
     value = kvb / step_s / 1e9
-    alg = algorithmic_bytes(words, total)
+    alg = algorithmic_bytes(words, total, fmt)
     achieved = alg / (avg_us * 1e-6) / 1e9
 
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, q, packed, scales, lens, args.cpu_budget)
+        cpu = cpu_baseline(w, q, packed, scales, lens, args.cpu_budget, fmt, kv_scale_host)
 
     line = {
-        "metric": "KV-cache HBM GB/s (us/call), MXFP4 MLA decode",
+        "metric": "KV-cache HBM GB/s (us/call), MXFP4 MLA decode" if fmt == "mxfp4"
+                  else f"KV-cache HBM GB/s (us/call), {fmt} MLA decode",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -231,11 +269,14 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 (MXFP4 e2m1/E8M0 KV, fp32 accumulate)",
+        "dtype": {"mxfp4": "bf16 (MXFP4 e2m1/E8M0 KV, fp32 accumulate)",
+                  "fp8": "bf16 (fp8 e4m3 KV + per-tensor scale, fp32 accumulate)",
+                  "bf16": "bf16 (bf16 KV, fp32 accumulate)"}[fmt],
         "data": "synthetic",
         "cold": bool(args.cold),
         "config": {
             "workload": w.name,
+            "kv_format": fmt,
             "batch": w.batch,
             "kv_len": w.kv_len if w.kv_len is not None else f"U{list(w.ragged)}",
             "total_tokens": total,
@@ -252,10 +293,11 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(w.name, fmt),
+            "kernel": KERNEL_NAME[fmt],
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "kernel_source_sha256": kernel_source_hash(),
+            "kernel_source_sha256": kernel_source_hash(fmt),
         },
         "cpu_baseline": cpu,
     }
