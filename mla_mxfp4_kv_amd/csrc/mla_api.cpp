@@ -41,6 +41,7 @@ struct PlanEntry {
   int device;
   int32_t num_slots;
   int32_t num_reduce;
+  int32_t wide_reduce;   // reduce kernel shape (see DecodeArgs)
   int32_t off_lse;
   int32_t off_out;
   size_t workspace_bytes;
@@ -152,7 +153,9 @@ int mla_plan_cus(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus, 
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan)");
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    g_plans[(uintptr_t)workspace] = PlanEntry{dev, p.num_slots, p.num_reduce, p.off_lse, p.off_out,
+    // more than 16 partials per merged sequence on average: the wide merge
+    const int32_t wide = p.num_partials > 16 * p.num_reduce ? 1 : 0;
+    g_plans[(uintptr_t)workspace] = PlanEntry{dev, p.num_slots, p.num_reduce, wide, p.off_lse, p.off_out,
                                               p.workspace_bytes};
   }
   return MLA_OK;
@@ -187,7 +190,10 @@ int mla_plan_device(const int32_t* kv_indptr_dev, int32_t batch, int64_t max_tot
     // the decode launches for the bounds; its kernels read the actual
     // counts from the plan words
     std::lock_guard<std::mutex> lk(g_mu);
-    g_plans[(uintptr_t)workspace] = PlanEntry{dev, (int32_t)l.slots, batch, (int32_t)l.off_lse,
+    // counts are only known on the device: a batch smaller than 1/16 of the
+    // slots may split its sequences into more than 16 partials each
+    const int32_t wide = (int64_t)batch * 16 < l.slots ? 1 : 0;
+    g_plans[(uintptr_t)workspace] = PlanEntry{dev, (int32_t)l.slots, batch, wide, (int32_t)l.off_lse,
                                               (int32_t)l.off_out, (size_t)l.total_bytes};
   }
   return MLA_OK;
@@ -249,6 +255,7 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   a.score_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.num_slots = pe.num_slots;
   a.num_reduce = pe.num_reduce;
+  a.wide_reduce = pe.wide_reduce;
   const int gmax = info.num_cus * MLA_PLAN_WG_PER_CU;
   a.grid = pe.num_slots < gmax ? pe.num_slots : gmax;
   hipError_t e;

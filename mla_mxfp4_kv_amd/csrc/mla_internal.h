@@ -74,6 +74,8 @@ struct DecodeArgs {
   int32_t num_slots;
   int32_t num_reduce;
   int32_t grid;            // decode workgroups to launch
+  int32_t wide_reduce;     // 1: merge with 16 waves per (sequence, head, dim quarter)
+                           // (long splits); 0: one wave per (sequence, head)
 };
 
 // GPU-side planner launch (mla_plan_kernel.hip).

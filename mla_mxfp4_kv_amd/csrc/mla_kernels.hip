@@ -680,7 +680,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 }
 
 // LSE-weighted merge of the partials of one sequence (or zero fill of an
-// empty one): out = sum_p 2^(lse_p - M) O_p / sum_p 2^(lse_p - M) with
+// empty one), for plans with long splits (many partials per sequence): out = sum_p 2^(lse_p - M) O_p / sum_p 2^(lse_p - M) with
 // M = max_p lse_p over non-empty partials. One workgroup per (reduce entry,
 // head, quarter of the 512 dims); its 16 waves take every 16th partial (so
 // a long split sequence is merged by many waves with their loads in flight)
@@ -761,6 +761,56 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
   }
 }
 
+// The same merge for plans whose split sequences have few partials each
+// (many sequences, a handful of splits): one 64-thread workgroup per
+// (reduce entry, head), each lane covering 8 consecutive output dims, so a
+// workgroup reads its partials with 16-byte loads and no LDS round. The
+// wide kernel above spreads one sequence's partials over 16 waves, which a
+// long split needs but which leaves most waves idle here.
+constexpr int kNarrowThreads = 64;
+static_assert(kVDim == 8 * kNarrowThreads, "narrow reduce: a lane covers 8 dims");
+
+__global__ void __launch_bounds__(kNarrowThreads)
+mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
+                         const float* __restrict__ part_out, uint16_t* __restrict__ out) {
+  if ((int)blockIdx.x >= plan[kPwNumReduce]) return;
+  const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
+  const int b = ent[0];
+  const int first = ent[1];
+  const int cnt = ent[2];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int d = 8 * lane;
+  u32x4_t* dst = (u32x4_t*)(out + ((size_t)b * kHeads + h) * kVDim + d);
+  if (cnt == 0) {
+    *dst = u32x4_t{0u, 0u, 0u, 0u};
+    return;
+  }
+  float m = kNegInf;
+  for (int i = lane; i < cnt; i += kNarrowThreads) {
+    const float v = part_lse[(size_t)(first + i) * kHeads + h];
+    if (v != kNegInf) m = fmaxf(m, v);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  float wsum = 0.f;
+  for (int i = 0; i < cnt; ++i) {
+    const float v = part_lse[(size_t)(first + i) * kHeads + h];
+    const f32x4_t* src = (const f32x4_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + d);
+    const f32x4_t o0 = src[0], o1 = src[1];
+    if (v != kNegInf) {
+      const float w = __builtin_amdgcn_exp2f(v - m);
+      wsum += w;
+      a0 += w * o0;
+      a1 += w * o1;
+    }
+  }
+  const float inv = wsum != 0.f ? 1.0f / wsum : 0.f;
+  *dst = u32x4_t{pack2(a0[0] * inv, a0[1] * inv), pack2(a0[2] * inv, a0[3] * inv),
+                 pack2(a1[0] * inv, a1[1] * inv), pack2(a1[2] * inv, a1[3] * inv)};
+}
+
 }  // namespace
 
 size_t decode_lds_bytes() { return (size_t)kLdsTotal; }
@@ -775,9 +825,13 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 
 int launch_reduce(const DecodeArgs& a, void* stream) {
   if (a.num_reduce <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce, kHeads, kReduceSplit), dim3(kReduceThreads), 0,
-                     (hipStream_t)stream,
-                     a.plan, a.part_lse, a.part_out, (uint16_t*)a.out);
+  if (a.wide_reduce) {
+    hipLaunchKernelGGL(mla_reduce_kernel, dim3(a.num_reduce, kHeads, kReduceSplit), dim3(kReduceThreads), 0,
+                       (hipStream_t)stream, a.plan, a.part_lse, a.part_out, (uint16_t*)a.out);
+  } else {
+    hipLaunchKernelGGL(mla_reduce_narrow_kernel, dim3(a.num_reduce, kHeads), dim3(kNarrowThreads), 0,
+                       (hipStream_t)stream, a.plan, a.part_lse, a.part_out, (uint16_t*)a.out);
+  }
   return (int)hipGetLastError();
 }
 
