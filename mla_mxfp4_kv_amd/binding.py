@@ -264,6 +264,19 @@ class MlaDecodeDevicePlan:
         decode(q, kv_packed, kv_scale, kv_indptr, out, sm_scale, self.workspace, stream)
         return out
 
+    def decode_fp8(self, q, kv_fp8, kv_scale, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0),
+                   stream=None):
+        """fp8-cache decode on the device plan (kv_fp8 uint8 [T,576], kv_scale float32 [1])."""
+        _validate_qo(q, out, self.batch)
+        decode_fp8(q, kv_fp8, kv_scale, kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+    def decode_bf16(self, q, kv_bf16, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        """bf16-cache decode on the device plan (kv_bf16 bfloat16 [T,576])."""
+        _validate_qo(q, out, self.batch)
+        decode_bf16(q, kv_bf16, kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
 
 def _validate_qo(q, out, batch):
     import torch

@@ -241,6 +241,59 @@ def test_errors():
     _check(out.float().cpu().numpy(), want, "after errors")
 
 
+def _indptr(lens):
+    out = [0]
+    for n in lens:
+        out.append(out[-1] + n)
+    return out
+
+
+def test_graph_replay_with_device_plan():
+    """GPU-side plan + fp8 decode + bf16 decode recorded in one HIP graph;
+    every replay follows the offsets in the device tensor at that moment and
+    matches the oracle."""
+    lens0 = [37, 1025, 0, 300, 2000]
+    steps = [lens0, [n + 1 for n in lens0], [n + 200 for n in lens0], [0, 0, 0, 0, 1]]
+    max_total = sum(steps[2])
+    batch = len(lens0)
+    q, c8, s8, _, _ = _inputs("fp8", [max_total], seed=35)
+    _, c16, _, _, _ = _inputs("bf16", [max_total], seed=35)
+    qb = torch.randn(batch, 16, 576, generator=torch.Generator().manual_seed(36)).to(torch.bfloat16)
+    qd, c8d, s8d, c16d = qb.cuda(), c8.cuda(), s8.cuda(), c16.cuda()
+    dp = binding.MlaDecodeDevicePlan(batch, max_total, num_cus=7)
+    kvi = torch.tensor(_indptr(steps[0]), dtype=torch.int32, device="cuda")
+    o8 = torch.empty(batch, 16, 512, dtype=torch.bfloat16, device="cuda")
+    o16 = torch.empty_like(o8)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dp.plan(kvi, stream=stream)
+        dp.decode_fp8(qd, c8d, s8d, kvi, o8, sm_scale=SM, stream=stream)
+        dp.decode_bf16(qd, c16d, kvi, o16, sm_scale=SM, stream=stream)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        dp.plan(kvi, stream=stream)
+        dp.decode_fp8(qd, c8d, s8d, kvi, o8, sm_scale=SM, stream=stream)
+        dp.decode_bf16(qd, c16d, kvi, o16, sm_scale=SM, stream=stream)
+    torch.cuda.synchronize()
+    qbits = _qbits(qb)
+    for k, lens in enumerate(steps):
+        _say(f"replay step {k} lens={lens}")
+        kvi.copy_(torch.tensor(_indptr(lens), dtype=torch.int32))
+        ind = np.array(_indptr(lens))
+        want8 = dref.mla_decode_ref_fp8(qbits, c8.numpy(), float(s8[0]), ind, SM)
+        want16 = dref.mla_decode_ref_bf16(qbits, _bits(c16), ind, SM)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            o8.fill_(7)
+            o16.fill_(7)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            _check(o8.float().cpu().numpy(), want8, f"fp8 step {k} replay {rep}")
+            _check(o16.float().cpu().numpy(), want16, f"bf16 step {k} replay {rep}")
+
+
 def _sampled_workload_check(fmt, name, sample):
     w = synth.WORKLOADS[name]
     _say(f"case {fmt} workload {name}: generating")
