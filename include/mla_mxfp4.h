@@ -165,6 +165,23 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                      const int32_t* kv_indptr, void* out, float sm_scale,
                      void* workspace, void* stream);
 
+/* The same decode over a cache whose rows are listed per token (page size
+ * 1): sequence b reads rows kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1] of
+ * the row pools kv_packed (uint8 [R, 288], 16-byte aligned) and kv_scale
+ * (uint8 [R, 18], 2-byte aligned) -- the kv_indices / page_size = 1 layout
+ * of the decode call on page "kernelbot-amd-mixed-mla-676098"
+ * (_aiter_mla_decode). kv_indices is int32 [kv_indptr[B]] on the device
+ * (4-byte aligned); entries before kv_indptr[0] are not read. Rows may be
+ * shared between sequences and appear in any order. Every index must lie
+ * in [0, R) and R * 288 must stay below 2^32 (offsets are 32-bit): the
+ * library cannot check this without reading the indices, so the caller
+ * guarantees it (the Python binding checks it). The plan is the one of
+ * mla_plan / mla_plan_device over the same kv_indptr; everything else as for
+ * mla_decode_mxfp4. */
+int mla_decode_mxfp4_paged(const void* q, const void* kv_packed, const void* kv_scale,
+                           const int32_t* kv_indices, const int32_t* kv_indptr, void* out,
+                           float sm_scale, void* workspace, void* stream);
+
 /* The same decode over an fp8 KV cache: kv_fp8 is uint8 [T, 576] (device,
  * 16-byte aligned), each byte an OCP FP8 E4M3 code (the MI355X fp8 type:
  * 4 exponent bits with bias 7, 3 mantissa bits, largest finite value 448,

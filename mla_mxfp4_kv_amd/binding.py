@@ -26,7 +26,7 @@ SCALES_PER_TOKEN = 18
 EXPORTS = (
     "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
     "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
-    "mla_decode_fp8", "mla_decode_bf16",
+    "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged",
 )
 
 _lib = None
@@ -63,13 +63,16 @@ def lib():
                                 c_sizep, c_sizep]
     L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_mxfp4_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                         ctypes.c_void_p]
     L.mla_decode_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
                  "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
-                 "mla_decode_bf16"):
+                 "mla_decode_bf16", "mla_decode_mxfp4_paged"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -151,6 +154,36 @@ def decode(q, kv_packed, kv_scale, kv_indptr_dev, out, sm_scale: float, workspac
         ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_mxfp4")
 
 
+def decode_mxfp4_paged(q, kv_packed, kv_scale, kv_indices, kv_indptr_dev, out, sm_scale: float, workspace,
+                       stream=None):
+    """Enqueue the MXFP4 decode over per-token row lists (no checks; see
+    ``MlaDecode.mxfp4_paged``)."""
+    _check(lib().mla_decode_mxfp4_paged(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_packed.data_ptr()),
+        ctypes.c_void_p(kv_scale.data_ptr()), ctypes.c_void_p(kv_indices.data_ptr()),
+        ctypes.c_void_p(kv_indptr_dev.data_ptr()), ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale),
+        ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_mxfp4_paged")
+
+
+def check_kv_indices(kv_indices, kv_indptr_host, pool_rows: int):
+    """Host-side guard for gathered caches: int32 contiguous device indices
+    covering kv_indptr[-1] tokens, all in [0, pool_rows) (reads the indices
+    back, one synchronisation), and a pool small enough for 32-bit offsets."""
+    import torch
+    if kv_indices.dtype != torch.int32 or kv_indices.dim() != 1 or not kv_indices.is_contiguous():
+        raise ValueError("kv_indices must be a contiguous int32 tensor")
+    hi_tok = int(kv_indptr_host[-1]) if len(kv_indptr_host) else 0
+    lo_tok = int(kv_indptr_host[0]) if len(kv_indptr_host) else 0
+    if kv_indices.numel() < hi_tok:
+        raise ValueError("kv_indices is shorter than kv_indptr[-1]")
+    if pool_rows * PACKED_BYTES >= 2 ** 32:
+        raise ValueError("the row pool must be smaller than 2^32 bytes")
+    if hi_tok > lo_tok:
+        used = kv_indices[lo_tok:hi_tok]
+        if int(used.min()) < 0 or int(used.max()) >= pool_rows:
+            raise ValueError("kv_indices holds rows outside the pool")
+
+
 def decode_fp8(q, kv_fp8, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
     """Enqueue the fp8-cache decode (``kv_scale``: float32 [1] device tensor)."""
     _check(lib().mla_decode_fp8(
@@ -197,6 +230,20 @@ class MlaDecode:
         if kv_packed.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode(q, kv_packed, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+    def mxfp4_paged(self, q, kv_packed, kv_scale, kv_indices, out=None, sm_scale=1.0 / math.sqrt(576.0),
+                    stream=None, check=True):
+        """Decode over row pools read through per-token indices (device int32
+        tensor); ``check`` verifies the indices against the pool first."""
+        import torch
+        if out is None:
+            out = torch.empty(self.batch, NUM_HEADS, V_DIM, dtype=torch.bfloat16, device=self.device)
+        _validate(q, kv_packed, kv_scale, out, self.batch)
+        if check:
+            check_kv_indices(kv_indices, self.indptr_host, kv_packed.shape[0])
+        decode_mxfp4_paged(q, kv_packed, kv_scale, kv_indices, self.kv_indptr, out, sm_scale, self.workspace,
+                           stream)
         return out
 
     def _out(self, q, out):

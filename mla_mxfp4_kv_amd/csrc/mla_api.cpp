@@ -213,7 +213,8 @@ enum class KvFormat { kMxfp4, kFp8, kBf16 };
 // Shared validation and launch of the three cache formats: the plan, the
 // partial layout and the reduce kernel are the same for all of them.
 int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_scale,
-                  const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
+                  const int32_t* kv_indices, const int32_t* kv_indptr, void* out, float sm_scale,
+                  void* workspace, void* stream, bool gather = false) {
   int dev;
   DeviceInfo info;
   int st = current_device(&dev, &info);
@@ -240,6 +241,12 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
     if (kv == nullptr || !aligned(kv, 16))
       return fail(MLA_ERR_INVALID, std::string(kv_name) + " must be non-null and 16-byte aligned");
     if (fmt == KvFormat::kMxfp4 && kv_scale == nullptr) return fail(MLA_ERR_INVALID, "kv_scale must be non-null");
+    if (gather) {
+      if (kv_indices == nullptr || !aligned(kv_indices, 4))
+        return fail(MLA_ERR_INVALID, "kv_indices must be a non-null 4-byte aligned device pointer");
+      if (fmt == KvFormat::kMxfp4 && !aligned(kv_scale, 2))
+        return fail(MLA_ERR_INVALID, "kv_scale must be 2-byte aligned for a gathered cache");
+    }
     if (fmt == KvFormat::kFp8 && (kv_scale == nullptr || !aligned(kv_scale, 4)))
       return fail(MLA_ERR_INVALID, "kv_scale must be a non-null 4-byte aligned device pointer");
   }
@@ -248,6 +255,7 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   a.kv_packed = (const uint8_t*)kv;
   a.kv_scale = (const uint8_t*)kv_scale;
   a.kv_indptr = kv_indptr;
+  a.kv_indices = gather ? kv_indices : nullptr;
   a.out = out;
   a.plan = (const int32_t*)workspace;
   a.part_lse = (float*)((uint8_t*)workspace + pe.off_lse);
@@ -278,18 +286,25 @@ extern "C" {
 int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                      const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
                      void* stream) {
-  return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, kv_indptr, out, sm_scale, workspace,
+  return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, nullptr, kv_indptr, out, sm_scale, workspace,
                        stream);
+}
+
+int mla_decode_mxfp4_paged(const void* q, const void* kv_packed, const void* kv_scale,
+                           const int32_t* kv_indices, const int32_t* kv_indptr, void* out, float sm_scale,
+                           void* workspace, void* stream) {
+  return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, kv_indices, kv_indptr, out, sm_scale,
+                       workspace, stream, true);
 }
 
 int mla_decode_fp8(const void* q, const void* kv_fp8, const float* kv_scale, const int32_t* kv_indptr,
                    void* out, float sm_scale, void* workspace, void* stream) {
-  return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, kv_indptr, out, sm_scale, workspace, stream);
+  return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, nullptr, kv_indptr, out, sm_scale, workspace, stream);
 }
 
 int mla_decode_bf16(const void* q, const void* kv_bf16, const int32_t* kv_indptr, void* out,
                     float sm_scale, void* workspace, void* stream) {
-  return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, kv_indptr, out, sm_scale, workspace, stream);
+  return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, nullptr, kv_indptr, out, sm_scale, workspace, stream);
 }
 
 }  // extern "C"

@@ -66,6 +66,7 @@ struct DecodeArgs {
   const uint8_t* kv_packed;
   const uint8_t* kv_scale;
   const int32_t* kv_indptr;
+  const int32_t* kv_indices;   // per-token cache rows (nullptr: contiguous sequences)
   void* out;
   const int32_t* plan;    // device plan words (workspace start)
   float* part_lse;

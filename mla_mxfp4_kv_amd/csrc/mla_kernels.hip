@@ -87,6 +87,24 @@ constexpr float kMInit = -1.0e30f;              // running max before the first 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 static_assert(kTile * kRowBytes % 1024 == 0, "a tile's rows are whole 1 KB DMA instructions");
 
+// LDS layout by cache addressing. kGather (rows listed per token in
+// kv_indices) keeps each tile row's scale bytes in a 32-byte slot of its own
+// (the two aligned 16-byte chunks that cover them) and the tile's 32 row
+// indices after them; the contiguous layout is the one above.
+template <bool kGather>
+struct Lds {
+  static constexpr int kBuf = kGather ? kLdsRaw + kTile * 32 + kTile * 4 : kLdsBuf;
+  static constexpr int kIdx = kLdsRaw + kTile * 32;
+  static constexpr int kPair = kNumBuf * kBuf;
+  static constexpr int kFmt = kPairs * kPair;
+  static constexpr int kXchg = kFmt + 2 * kPairs * kFmtTile;
+  static constexpr int kMain = kXchg + 2 * kPairs * 64 * 32;
+  static constexpr int kTotal = kMain > kMergeBytes ? kMain : kMergeBytes;
+};
+static_assert(Lds<false>::kTotal == kLdsTotal, "contiguous layout unchanged");
+static_assert(Lds<true>::kTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
+static_assert(Lds<true>::kBuf % 64 == 0, "buffers stay 64-byte aligned");
+
 // Stage one 32-token tile into an LDS buffer with direct global->LDS loads
 // (a 16-byte DMA instruction writes 64 consecutive 16-byte LDS slots, lane i
 // -> slot i, each lane choosing its global source):
@@ -148,6 +166,66 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
   stage_dma<0, kRowDma, true>(buf, kv, sc, t0, nvalid, lane);
 }
 
+// Row indices of the tile starting at token t0 (kv_indices[t0 .. t0 + 31],
+// the last valid one repeated past the item's end) into the buffer's index
+// slot: one 4-byte direct load per lane of the first 32.
+__device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restrict__ kv_indices, int t0,
+                                          int nvalid, int lane) {
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  if (lane < kTile) {
+    const int r = min(lane, nvalid - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(kv_indices + t0 + r),
+                                     (MLA_LDS void*)(buf + Lds<true>::kIdx), 4, 0, 0);
+  }
+}
+
+// Stage a tile whose rows are listed in the buffer's index slot: lane chunk
+// c = 64*i + lane of instruction i is 16-byte chunk c % 18 of tile row c / 18
+// (rows past the item's end repeat the last valid row's last chunk); each
+// row's 18 scale bytes come as the two aligned 16-byte chunks that cover
+// them (an 18-byte row starts at an even offset, so two always suffice)
+// into the row's 32-byte slot. All indices are read before any load is
+// issued.
+__device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __restrict__ kv,
+                                             const uint8_t* __restrict__ sc, int nvalid, int lane) {
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const int last = min(nvalid, kTile) - 1;
+  const int32_t* idx = (const int32_t*)(buf + Lds<true>::kIdx);
+  uint32_t off[kRowDma];
+#pragma unroll
+  for (int i = 0; i < kRowDma; ++i) {
+    const int c = 64 * i + lane;
+    int r = c / 18;
+    int w = c - 18 * r;
+    if (r > last) {
+      r = last;
+      w = 17;
+    }
+    off[i] = (uint32_t)idx[r] * (uint32_t)kRowBytes + 16u * (uint32_t)w;
+  }
+  const uintptr_t srow = (uintptr_t)(sc + (size_t)(uint32_t)idx[min(lane >> 1, last)] * kBlocks);
+#pragma unroll
+  for (int i = 0; i < kRowDma; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(kv + off[i]), (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void*)((srow & ~(uintptr_t)15) + 16 * (uintptr_t)(lane & 1)),
+                                   (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
+}
+
+// LDS address of the scale bytes of tile row `row`. delta: in the
+// contiguous layout the offset of the tile's first scale byte in its
+// 16-byte chunk; with kGather the offset of the scale array's base in its
+// chunk (row p starts 18 p = 2 p mod 16 bytes after it).
+template <bool kGather>
+__device__ __forceinline__ const uint8_t* scale_row(const uint8_t* buf, int delta, int row) {
+  if constexpr (kGather) {
+    const int32_t* idx = (const int32_t*)(buf + Lds<true>::kIdx);
+    return buf + kLdsRaw + 32 * row + ((delta + 2 * idx[row]) & 15);
+  } else {
+    return buf + kLdsRaw + delta + kBlocks * row;
+  }
+}
+
 // Rewrite the V scales of a landed tile as exponent-field dwords (e << 23,
 // the form the fp4 converter takes as its scale operand) into `fmt`
 // ([block][position]). Position 8g + j of a block is token 4g + j of the
@@ -156,21 +234,30 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
 // `l` (0..127) picks one block and four consecutive positions. Rows at or
 // past `nvalid` get scale 1 (their p is 0, and a stale byte must not turn
 // 0 * V into NaN).
+template <bool kGather>
 __device__ __forceinline__ void format_scales(const uint8_t* buf, uint8_t* fmt, int delta,
                                               int nvalid, int l) {
   const int blk = l >> 3;
   const int pg = l & 7;
   const int row0 = 16 * (pg & 1) + 4 * (pg >> 1);
-  const uint8_t* raw = buf + kLdsRaw + delta + blk;
   u32x4_t v;
-  if (nvalid >= kTile) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = (uint32_t)raw[kBlocks * (row0 + j)] << 23;
-  } else {
+  if constexpr (kGather) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t e = raw[kBlocks * (row0 + j)];
+      const uint32_t e = scale_row<true>(buf, delta, row0 + j)[blk];
       v[j] = row0 + j < nvalid ? e << 23 : 127u << 23;
+    }
+  } else {
+    const uint8_t* raw = buf + kLdsRaw + delta + blk;
+    if (nvalid >= kTile) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (uint32_t)raw[kBlocks * (row0 + j)] << 23;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t e = raw[kBlocks * (row0 + j)];
+        v[j] = row0 + j < nvalid ? e << 23 : 127u << 23;
+      }
     }
   }
   *(u32x4_t*)(fmt + blk * (kTile * 4) + 16 * pg) = v;
@@ -371,6 +458,7 @@ __device__ __forceinline__ f32x4_t mx_chunk(const u32x4_t& k, uint32_t k_scale, 
 
 // S^T = K Q^T for one 16-token sub-tile: returns, for head `col`, the raw
 // scores of tokens 16*sub + 4*grp + r (r = 0..3).
+template <bool kGather>
 __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int delta, int sub,
                                               const QOperands& qo, int lane) {
   const int col = lane & 15;
@@ -381,7 +469,7 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int delta, int
 #pragma unroll
   for (int m = 0; m < 4; ++m) c[m] = *(const u32x4_t*)(rp + 16 * (4 * m + grp));
   const u32x2_t rope = *(const u32x2_t*)(rp + 256 + 8 * grp);
-  const uint8_t* er = buf + kLdsRaw + delta + kBlocks * row;
+  const uint8_t* er = scale_row<kGather>(buf, delta, row);
   uint32_t e[5];
 #pragma unroll
   for (int m = 0; m < 4; ++m) e[m] = er[4 * m + grp];
@@ -517,12 +605,15 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
   pv_block<0>(tra, sca, v_cur, s_lo, s_hi, pa, o);
 }
 
+template <bool kGather>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
-                  uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
-                  float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
+                  const int32_t* __restrict__ kv_indices, uint16_t* __restrict__ out,
+                  const int32_t* __restrict__ plan, float* __restrict__ part_lse,
+                  float* __restrict__ part_out, float csc) {
+  using L = Lds<kGather>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kTotal];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & 3;
@@ -534,9 +625,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int num_slots = plan[kPwNumSlots];
   const int32_t* slot_indptr = plan + plan[kPwOffSlot];
   const int32_t* items = plan + plan[kPwOffItems];
-  uint8_t* ring = lds + pair * kLdsPair;
-  TileHandoff* hand = (TileHandoff*)(lds + kLdsXchg) + pair * 64 + lane;  // + parity * kPairs * 64
-  uint8_t* fmt_pair = lds + kLdsFmt + pair * kFmtTile;  // + parity * kPairs * kFmtTile
+  uint8_t* ring = lds + pair * L::kPair;
+  TileHandoff* hand = (TileHandoff*)(lds + L::kXchg) + pair * 64 + lane;  // + parity * kPairs * 64
+  uint8_t* fmt_pair = lds + L::kFmt + pair * kFmtTile;  // + parity * kPairs * kFmtTile
   // The scorer's results gate the next round of both waves: it gets issue
   // priority over the P V wave on the shared SIMD.
   if (scorer) __builtin_amdgcn_s_setprio(1);
@@ -573,25 +664,46 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         st.m = kMInit;
         const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp);
         __syncthreads();  // LDS of the previous item's merge is free again
-        if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
+        if (ntiles > 0) {
+          if constexpr (kGather) {
+            // row indices of the first two tiles, then tile 0 from them
+            stage_idx(ring, kv_indices, t_first, ke - t_first, lane);
+            if (ntiles > 1)
+              stage_idx(ring + L::kBuf, kv_indices, t_first + kTileStride, ke - t_first - kTileStride, lane);
+            wait_dma();
+            stage_gather(ring, kv, sc, ke - t_first, lane);
+          } else {
+            stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
+          }
+        }
         for (int i = 0; i <= rounds; ++i) {
           const bool qk_on = i < ntiles;
           if (qk_on) wait_dma();
           __syncthreads();  // tile i landed; tile i-2 fully consumed; hand-off of i-1 visible
           if (i + 1 < ntiles) {
             const int tn = t_first + (i + 1) * kTileStride;
-            stage_dma(ring + ((i + 1) % kNumBuf) * kLdsBuf, kv, sc, tn, ke - tn, lane);
+            if constexpr (kGather) {
+              // tile i + 1 from the indices staged a round ago; the indices
+              // of tile i + 2 go to the slot of the buffer it will use (the
+              // P V wave reads only that buffer's rows this round)
+              stage_gather(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, ke - tn, lane);
+              if (i + 2 < ntiles)
+                stage_idx(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, tn + kTileStride,
+                          ke - tn - kTileStride, lane);
+            } else {
+              stage_dma(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn, ke - tn, lane);
+            }
           }
           if (qk_on) {
             const int tq = t_first + i * kTileStride;
-            const uint8_t* bq = ring + (i % kNumBuf) * kLdsBuf;
-            const int dq = raw_delta(sc, tq);
-            const f32x4_t s0 = qk_subtile(bq, dq, 0, qo, lane);
-            const f32x4_t s1 = qk_subtile(bq, dq, 1, qo, lane);
+            const uint8_t* bq = ring + (i % kNumBuf) * L::kBuf;
+            const int dq = kGather ? (int)((uintptr_t)sc & 15) : raw_delta(sc, tq);
+            const f32x4_t s0 = qk_subtile<kGather>(bq, dq, 0, qo, lane);
+            const f32x4_t s1 = qk_subtile<kGather>(bq, dq, 1, qo, lane);
             hand[(i & 1) * (kPairs * 64)] = softmax_tile(s0, s1, tq, ke, st, csc, lane);
             uint8_t* fm = fmt_pair + (i & 1) * (kPairs * kFmtTile);
-            format_scales(bq, fm, dq, ke - tq, lane);
-            format_scales(bq, fm, dq, ke - tq, 64 + lane);
+            format_scales<kGather>(bq, fm, dq, ke - tq, lane);
+            format_scales<kGather>(bq, fm, dq, ke - tq, 64 + lane);
           }
         }
         __syncthreads();  // all rounds done: the ring area is free for the merge
@@ -609,7 +721,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           __syncthreads();
           if (i >= 1 && i - 1 < ntiles) {
             const TileHandoff h = hand[((i - 1) & 1) * (kPairs * 64)];
-            pv_tile(ring + ((i - 1) % kNumBuf) * kLdsBuf, fmt_pair + ((i - 1) & 1) * (kPairs * kFmtTile),
+            pv_tile(ring + ((i - 1) % kNumBuf) * L::kBuf, fmt_pair + ((i - 1) & 1) * (kPairs * kFmtTile),
                     h, o, lane);
           }
         }
@@ -813,13 +925,19 @@ mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restri
 
 }  // namespace
 
-size_t decode_lds_bytes() { return (size_t)kLdsTotal; }
+size_t decode_lds_bytes() { return (size_t)Lds<true>::kTotal; }
 
 int launch_decode(const DecodeArgs& a, void* stream) {
   if (a.num_slots <= 0 || a.grid <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL(mla_decode_kernel, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
-                     (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (uint16_t*)a.out,
-                     a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+  if (a.kv_indices != nullptr) {
+    hipLaunchKernelGGL(mla_decode_kernel<true>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, a.kv_indices,
+                       (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+  } else {
+    hipLaunchKernelGGL(mla_decode_kernel<false>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (const int32_t*)nullptr,
+                       (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+  }
   return (int)hipGetLastError();
 }
 

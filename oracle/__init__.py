@@ -43,6 +43,7 @@ from .mxfp4_ref import (  # noqa: F401
     dequant_mxfp4,
     mla_decode_ref,
     mla_decode_ref_seq,
+    mla_decode_ref_gather,
 )
 from .dense_ref import (  # noqa: F401
     E4M3_VALUES,

@@ -141,3 +141,21 @@ def mla_decode_ref(q, packed, scales, kv_indptr, sm_scale: float,
         lo, hi = int(indptr[b]), int(indptr[b + 1])
         out[b] = mla_decode_ref_seq(q[b], packed[lo:hi], scales[lo:hi], sm_scale)
     return out
+
+
+def mla_decode_ref_gather(q, packed, scales, kv_indices, kv_indptr, sm_scale: float,
+                          batches=None) -> np.ndarray:
+    """Oracle for a cache whose token rows are listed per token: sequence b
+    reads rows ``kv_indices[kv_indptr[b] : kv_indptr[b+1]]`` of the row pool
+    (page size 1, the layout the decode call on page
+    "kernelbot-amd-mixed-mla-676098" describes with ``kv_indices`` and
+    ``page_size=1``). Otherwise the same definition: float64 [B, 16, 512]."""
+    indptr = np.asarray(kv_indptr, dtype=np.int64)
+    idx = np.asarray(kv_indices, dtype=np.int64)
+    nb = indptr.shape[0] - 1
+    q = np.asarray(q)
+    out = np.full((nb, NUM_HEADS, V_DIM), np.nan, dtype=np.float64)
+    for b in (range(nb) if batches is None else batches):
+        rows = idx[int(indptr[b]):int(indptr[b + 1])]
+        out[b] = mla_decode_ref_seq(q[b], np.asarray(packed)[rows], np.asarray(scales)[rows], sm_scale)
+    return out

@@ -1,0 +1,174 @@
+"""GPU parity of the MXFP4 decode over per-token row lists
+(mla_decode_mxfp4_paged, page size 1) against the fp64 oracle, through the
+C ABI. Same bar as the contiguous decode."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mla_mxfp4_kv_amd import binding, synth
+from oracle import mxfp4_ref as ref
+
+pytestmark = pytest.mark.gpu
+
+SM = 1.0 / math.sqrt(576.0)
+ATOL = 1e-2
+RTOL = 1e-2
+NORMWISE = 5e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+    yield
+
+
+def _qbits(q):
+    return q.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check(got, want, label):
+    nan_w = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan_w), f"{label}: NaN pattern differs"
+    g, w = got[~nan_w], want[~nan_w]
+    err = np.abs(g - w)
+    assert np.all(err <= ATOL + RTOL * np.abs(w)), f"{label}: max err {float(err.max()):.3e}"
+    den = np.linalg.norm(w)
+    if den > 0:
+        nw = np.linalg.norm(g - w) / den
+        assert nw <= NORMWISE, f"{label}: normwise {nw:.3e}"
+
+
+def _case(lens, seed, extra=2.0):
+    """Contiguous inputs plus a row pool `extra` times larger holding the
+    same rows at random positions (the rest random bytes), and the indices."""
+    w = synth.Workload("g", len(lens), None, None, 1.0, False, seed)
+    q, packed, scales, indptr, _ = synth.make_inputs(w, lengths=lens)
+    t = int(indptr[-1])
+    rng = np.random.default_rng(seed)
+    rows = max(1, int(extra * t))
+    pos = torch.from_numpy(rng.permutation(rows)[:t].astype(np.int32))
+    pool_p = torch.from_numpy(rng.integers(0, 256, (rows, 288), dtype=np.uint8))
+    pool_s = torch.from_numpy(rng.integers(118, 136, (rows, 18), dtype=np.uint8))
+    pool_p[pos.long()] = packed
+    pool_s[pos.long()] = scales
+    return q, packed, scales, indptr, pool_p, pool_s, pos
+
+
+CASES = [
+    ([1], 0),
+    ([31, 32, 33], 0),
+    ([127, 128, 129], 3),
+    ([0, 300, 0, 1000], 0),
+    ([5000], 0),
+    ([1, 1, 1, 1, 700], 7),
+    ([257, 4097, 33, 2000], 0),
+]
+
+
+@pytest.mark.parametrize("lens,num_cus", CASES)
+def test_gather_matches_oracle(lens, num_cus):
+    _say(f"case gather lens={lens} num_cus={num_cus}")
+    q, packed, scales, indptr, pool_p, pool_s, pos = _case(lens, seed=sum(lens) + 5)
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=num_cus)
+    out = dec.mxfp4_paged(q.cuda(), pool_p.cuda(), pool_s.cuda(), pos.cuda(), sm_scale=SM)
+    torch.cuda.synchronize()
+    want = ref.mla_decode_ref_gather(_qbits(q), pool_p.numpy(), pool_s.numpy(), pos.numpy(),
+                                     indptr.numpy(), SM)
+    _check(out.float().cpu().numpy(), want, f"gather {lens}")
+
+
+def test_identity_rows_are_bit_identical_to_contiguous():
+    """kv_indices = arange: the same values in the same order through the same
+    plan, so the output equals the contiguous decode bit for bit."""
+    _say("case gather identity")
+    lens = [700, 33, 4100]
+    w = synth.Workload("g", len(lens), None, None, 1.0, False, 17)
+    q, packed, scales, indptr, _ = synth.make_inputs(w, lengths=lens)
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=9)
+    qd, pd, sd = q.cuda(), packed.cuda(), scales.cuda()
+    a = dec(qd, pd, sd, sm_scale=SM).clone()
+    ident = torch.arange(int(indptr[-1]), dtype=torch.int32, device="cuda")
+    b = dec.mxfp4_paged(qd, pd, sd, ident, sm_scale=SM)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_shared_rows_and_misaligned_scale_pool():
+    """Two sequences reading the same rows (a shared prefix), with the scale
+    pool starting 2 and 6 bytes past an aligned address."""
+    _say("case gather shared rows, scale pool offsets")
+    lens = [500, 300, 64]
+    q, packed, scales, indptr, pool_p, pool_s, pos = _case(lens, seed=23)
+    pos = pos.clone()
+    pos[500:600] = pos[0:100]          # sequence 1 starts with sequence 0's first 100 rows
+    want = ref.mla_decode_ref_gather(_qbits(q), pool_p.numpy(), pool_s.numpy(), pos.numpy(),
+                                     indptr.numpy(), SM)
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=4)
+    for shift in (2, 6):
+        flat = torch.zeros(pool_s.numel() + 16, dtype=torch.uint8)
+        flat[shift:shift + pool_s.numel()] = pool_s.reshape(-1)
+        sd = flat.cuda()[shift:shift + pool_s.numel()].view(-1, 18)
+        out = dec.mxfp4_paged(q.cuda(), pool_p.cuda(), sd, pos.cuda(), sm_scale=SM)
+        torch.cuda.synchronize()
+        _check(out.float().cpu().numpy(), want, f"shared rows, scale shift {shift}")
+
+
+def test_gather_errors():
+    _say("case gather errors")
+    q, packed, scales, indptr, pool_p, pool_s, pos = _case([40], seed=29)
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda")
+    qd, pd, sd, idx = q.cuda(), pool_p.cuda(), pool_s.cuda(), pos.cuda()
+    with pytest.raises(ValueError):
+        dec.mxfp4_paged(qd, pd, sd, idx + pool_p.shape[0], sm_scale=SM)   # rows outside the pool
+    with pytest.raises(ValueError):
+        dec.mxfp4_paged(qd, pd, sd, idx[:10], sm_scale=SM)                # too few indices
+    out = torch.empty(1, 16, 512, dtype=torch.bfloat16, device="cuda")
+    L = binding.lib()
+    ptr = lambda t: binding.ctypes.c_void_p(t.data_ptr())
+    st = L.mla_decode_mxfp4_paged(ptr(qd), ptr(pd), ptr(sd), None, ptr(dec.kv_indptr), ptr(out), SM,
+                                  ptr(dec.workspace), None)
+    assert st == -1
+    flat = torch.zeros(sd.numel() + 16, dtype=torch.uint8, device="cuda")
+    odd = flat[1:1 + sd.numel()]
+    st = L.mla_decode_mxfp4_paged(ptr(qd), ptr(pd), ptr(odd), ptr(idx), ptr(dec.kv_indptr), ptr(out), SM,
+                                  ptr(dec.workspace), None)
+    assert st == -1
+
+
+def test_gather_workload_b256_page_shuffled():
+    """The headline workload with its rows scattered over the pool in 16-row
+    pages (a paged cache), checked on sampled sequences."""
+    w = synth.WORKLOADS["b256_kv8192"]
+    _say("case gather b256_kv8192: generating")
+    q, packed, scales, indptr, lens = synth.make_inputs(w, device="cuda")
+    t = int(indptr[-1])
+    g = torch.Generator(device="cpu").manual_seed(99)
+    perm = torch.randperm(t // 16, generator=g).to(torch.int32)
+    idx = (perm.repeat_interleave(16) * 16 + torch.arange(16, dtype=torch.int32).repeat(t // 16)).cuda()
+    pool_p = torch.empty_like(packed)
+    pool_s = torch.empty_like(scales)
+    pool_p[idx.long()] = packed
+    pool_s[idx.long()] = scales
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda")
+    _say("case gather b256_kv8192: decode")
+    out = dec.mxfp4_paged(q, pool_p, pool_s, idx, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    qb = _qbits(q)
+    ind = indptr.numpy()
+    for b in (0, 131, 255):
+        lo, hi = int(ind[b]), int(ind[b + 1])
+        want = ref.mla_decode_ref_seq(qb[b], packed[lo:hi].cpu().numpy(), scales[lo:hi].cpu().numpy(), w.sm_scale)
+        _check(got[b], want, f"b256 gather b={b}")
+    assert np.all(np.isfinite(got))

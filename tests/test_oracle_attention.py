@@ -193,3 +193,32 @@ def test_v_is_first_512_dims_not_rope():
     p2[0, 256:] ^= 0x11
     got = ref.mla_decode_ref(qbits, p2, scales, indptr, SM)
     assert np.array_equal(base, got)
+
+
+def test_gather_oracle_matches_contiguous():
+    """Per-token row lists: identity rows, a permuted pool read through the
+    inverse permutation, and rows shared by two sequences all reduce to the
+    contiguous definition on the rows actually read."""
+    rng = np.random.default_rng(41)
+    lens = [3, 0, 7, 2]
+    qbits, packed, scales, indptr = _rand_case(rng, lens)
+    t = int(indptr[-1])
+    want = ref.mla_decode_ref(qbits, packed, scales, indptr, SM)
+    ident = np.arange(t, dtype=np.int32)
+    assert np.array_equal(ref.mla_decode_ref_gather(qbits, packed, scales, ident, indptr, SM), want)
+    # pool of 3t rows: row i of the contiguous cache sits at pool row pos[i]
+    pos = rng.permutation(3 * t)[:t].astype(np.int32)
+    pool_p = rng.integers(0, 256, (3 * t, 288), dtype=np.uint8)
+    pool_s = rng.integers(122, 131, (3 * t, 18), dtype=np.uint8)
+    pool_p[pos] = packed
+    pool_s[pos] = scales
+    assert np.array_equal(ref.mla_decode_ref_gather(qbits, pool_p, pool_s, pos, indptr, SM), want)
+    # sequence 3 reads the first two rows of sequence 0 (a shared prefix)
+    shared = ident.copy()
+    shared[indptr[3]:indptr[4]] = [0, 1]
+    got = ref.mla_decode_ref_gather(qbits, packed, scales, shared, indptr, SM)
+    copy_p, copy_s = packed.copy(), scales.copy()
+    copy_p[indptr[3]:indptr[4]] = packed[0:2]
+    copy_s[indptr[3]:indptr[4]] = scales[0:2]
+    np.testing.assert_array_equal(got, ref.mla_decode_ref(qbits, copy_p, copy_s, indptr, SM))
+    assert not np.array_equal(got[3], want[3])
