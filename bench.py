@@ -30,7 +30,7 @@ KERNEL_SRC = {
     "fp8": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
     "bf16": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
 }
-KERNEL_NAME = {"mxfp4": "mla_decode_kernel", "fp8": "mla_decode_dense_kernel<true>",
+KERNEL_NAME = {"mxfp4": "mla_decode_kernel<false>", "fp8": "mla_decode_dense_kernel<true>",
                "bf16": "mla_decode_dense_kernel<false>"}
 
 
@@ -79,13 +79,14 @@ QO_BYTES_PER_SEQ = 16 * 576 * 2 + 16 * 512 * 2
 PARTIAL_BYTES = 16 * (512 + 1) * 4
 
 
-def algorithmic_bytes(words, total_tokens, fmt="mxfp4"):
-    """Bytes the decode must move: KV (+ scales), Q, output, and each split
-    partial written once and read once."""
+def algorithmic_bytes(words, total_tokens, fmt="mxfp4", gather=False):
+    """Bytes the decode must move: KV (+ scales), Q, output, each split
+    partial written once and read once, and with a gathered cache the
+    4-byte row index of every token."""
     num_partials = words[9]
     batch = words[2]
     return (synth.kv_bytes(total_tokens, fmt) + batch * QO_BYTES_PER_SEQ
-            + 2 * num_partials * PARTIAL_BYTES)
+            + 2 * num_partials * PARTIAL_BYTES + (4 * total_tokens if gather else 0))
 
 
 def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=None):
@@ -145,6 +146,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="b256_kv8192", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--kv-format", default="mxfp4", choices=["mxfp4", "fp8", "bf16"],
                     help="cache format: the MXFP4 headline path, or the fp8 / bf16 sibling decodes")
+    ap.add_argument("--gather", type=int, default=0, metavar="PAGE",
+                    help="MXFP4 only: scatter the rows over the pool in pages of PAGE rows (seeded "
+                         "shuffle) and decode through per-token kv_indices (mla_decode_mxfp4_paged)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
@@ -182,7 +186,31 @@ def main(argv=None):
     plan_ms = (time.perf_counter() - t_plan) * 1e3
     words, _ = binding.plan_host(indptr.tolist(), binding.num_cus())
     out = torch.empty(w.batch, 16, 512, dtype=torch.bfloat16, device=dev)
-    if fmt == "mxfp4":
+    kv_indices = None
+    if args.gather:
+        if fmt != "mxfp4":
+            print("--gather is built for the MXFP4 decode only", file=sys.stderr)
+            return 2
+        page = args.gather
+        if total % page:
+            print(f"--gather {page}: the token count {total} is not a multiple of the page", file=sys.stderr)
+            return 2
+        g = torch.Generator().manual_seed(1234)
+        perm = torch.randperm(total // page, generator=g).to(torch.int32)
+        kv_indices = (perm.repeat_interleave(page) * page
+                      + torch.arange(page, dtype=torch.int32).repeat(total // page)).to(dev)
+        pool_p = torch.empty_like(packed)
+        pool_s = torch.empty_like(scales)
+        pool_p[kv_indices.long()] = packed
+        pool_s[kv_indices.long()] = scales
+        packed, scales = pool_p, pool_s
+        binding.check_kv_indices(kv_indices, indptr.tolist(), packed.shape[0])
+        torch.cuda.synchronize()
+    if kv_indices is not None:
+        def call():
+            binding.decode_mxfp4_paged(q, packed, scales, kv_indices, dec.kv_indptr, out, w.sm_scale,
+                                       dec.workspace)
+    elif fmt == "mxfp4":
         def call():
             dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
     elif fmt == "fp8":
@@ -244,7 +272,7 @@ def main(argv=None):
     # wall clock includes the flushes, so the event time is used instead
     step_s = (avg_us * 1e-6) if args.cold else (wall / args.steps)
     value = kvb / step_s / 1e9
-    alg = algorithmic_bytes(words, total, fmt)
+    alg = algorithmic_bytes(words, total, fmt, kv_indices is not None)
     achieved = alg / (avg_us * 1e-6) / 1e9
 
     cpu = None
@@ -277,6 +305,7 @@ def main(argv=None):
         "config": {
             "workload": w.name,
             "kv_format": fmt,
+            "gather_page_rows": args.gather or None,
             "batch": w.batch,
             "kv_len": w.kv_len if w.kv_len is not None else f"U{list(w.ragged)}",
             "total_tokens": total,
@@ -293,8 +322,8 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, fmt),
-            "kernel": KERNEL_NAME[fmt],
+            "traffic": None if args.gather else measured_traffic(w.name, fmt),
+            "kernel": "mla_decode_kernel<true>" if args.gather else KERNEL_NAME[fmt],
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_source_sha256": kernel_source_hash(fmt),

@@ -20,7 +20,8 @@ Sources (kernelindex.com "amd-mixed-mla" leaderboard submission pages):
 
 Modules:
 
-* :mod:`oracle.mxfp4_ref` -- exact MXFP4 dequantisation and fp64 attention.
+* :mod:`oracle.mxfp4_ref` -- exact MXFP4 dequantisation and fp64 attention,
+  also over per-token row lists (``mla_decode_ref_gather``).
 * :mod:`oracle.dense_ref` -- exact fp8 (e4m3 + per-tensor scale) and bf16
   cache decoding and the same fp64 attention, for the sibling decodes.
 * :mod:`oracle.planner_ref` -- the CPU reference work-list planner.
