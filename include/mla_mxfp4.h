@@ -204,6 +204,19 @@ int mla_decode_fp8(const void* q, const void* kv_fp8, const float* kv_scale,
 int mla_decode_bf16(const void* q, const void* kv_bf16, const int32_t* kv_indptr,
                     void* out, float sm_scale, void* workspace, void* stream);
 
+/* mla_decode_fp8 and mla_decode_bf16 over per-token row lists: sequence b
+ * reads rows kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1] of the row pool
+ * (fp8: uint8 [R, 576]; bf16: bfloat16 [R, 576]; 16-byte aligned), with the
+ * rules of mla_decode_mxfp4_paged: kv_indices int32 on the device, 4-byte
+ * aligned, every index in [0, R), R * row bytes below 2^32, checked by the
+ * caller. */
+int mla_decode_fp8_paged(const void* q, const void* kv_fp8, const float* kv_scale,
+                         const int32_t* kv_indices, const int32_t* kv_indptr, void* out,
+                         float sm_scale, void* workspace, void* stream);
+int mla_decode_bf16_paged(const void* q, const void* kv_bf16, const int32_t* kv_indices,
+                          const int32_t* kv_indptr, void* out, float sm_scale,
+                          void* workspace, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ SCALES_PER_TOKEN = 18
 EXPORTS = (
     "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
     "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
-    "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged",
+    "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
+    "mla_decode_bf16_paged",
 )
 
 _lib = None
@@ -66,13 +67,16 @@ def lib():
     L.mla_decode_mxfp4_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                                          ctypes.c_void_p]
+    L.mla_decode_fp8_paged.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_bf16_paged.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
                  "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
-                 "mla_decode_bf16", "mla_decode_mxfp4_paged"):
+                 "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
+                 "mla_decode_bf16_paged"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -165,7 +169,26 @@ def decode_mxfp4_paged(q, kv_packed, kv_scale, kv_indices, kv_indptr_dev, out, s
         ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_mxfp4_paged")
 
 
-def check_kv_indices(kv_indices, kv_indptr_host, pool_rows: int):
+def decode_fp8_paged(q, kv_fp8, kv_scale, kv_indices, kv_indptr_dev, out, sm_scale: float, workspace,
+                     stream=None):
+    """Enqueue the fp8 decode over per-token row lists (no checks)."""
+    _check(lib().mla_decode_fp8_paged(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_fp8.data_ptr()), ctypes.c_void_p(kv_scale.data_ptr()),
+        ctypes.c_void_p(kv_indices.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()),
+        _stream_ptr(stream)), "mla_decode_fp8_paged")
+
+
+def decode_bf16_paged(q, kv_bf16, kv_indices, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
+    """Enqueue the bf16 decode over per-token row lists (no checks)."""
+    _check(lib().mla_decode_bf16_paged(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_bf16.data_ptr()),
+        ctypes.c_void_p(kv_indices.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()),
+        _stream_ptr(stream)), "mla_decode_bf16_paged")
+
+
+def check_kv_indices(kv_indices, kv_indptr_host, pool_rows: int, row_bytes: int = PACKED_BYTES):
     """Host-side guard for gathered caches: int32 contiguous device indices
     covering kv_indptr[-1] tokens, all in [0, pool_rows) (reads the indices
     back, one synchronisation), and a pool small enough for 32-bit offsets."""
@@ -176,7 +199,7 @@ def check_kv_indices(kv_indices, kv_indptr_host, pool_rows: int):
     lo_tok = int(kv_indptr_host[0]) if len(kv_indptr_host) else 0
     if kv_indices.numel() < hi_tok:
         raise ValueError("kv_indices is shorter than kv_indptr[-1]")
-    if pool_rows * PACKED_BYTES >= 2 ** 32:
+    if pool_rows * row_bytes >= 2 ** 32:
         raise ValueError("the row pool must be smaller than 2^32 bytes")
     if hi_tok > lo_tok:
         used = kv_indices[lo_tok:hi_tok]
@@ -244,6 +267,24 @@ class MlaDecode:
             check_kv_indices(kv_indices, self.indptr_host, kv_packed.shape[0])
         decode_mxfp4_paged(q, kv_packed, kv_scale, kv_indices, self.kv_indptr, out, sm_scale, self.workspace,
                            stream)
+        return out
+
+    def fp8_paged(self, q, kv_fp8, kv_scale, kv_indices, out=None, sm_scale=1.0 / math.sqrt(576.0),
+                  stream=None, check=True):
+        """fp8 decode over a row pool read through per-token indices."""
+        out = self._out(q, out)
+        if check:
+            check_kv_indices(kv_indices, self.indptr_host, kv_fp8.shape[0], QK_DIM)
+        decode_fp8_paged(q, kv_fp8, kv_scale, kv_indices, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+    def bf16_paged(self, q, kv_bf16, kv_indices, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None,
+                   check=True):
+        """bf16 decode over a row pool read through per-token indices."""
+        out = self._out(q, out)
+        if check:
+            check_kv_indices(kv_indices, self.indptr_host, kv_bf16.shape[0], 2 * QK_DIM)
+        decode_bf16_paged(q, kv_bf16, kv_indices, self.kv_indptr, out, sm_scale, self.workspace, stream)
         return out
 
     def _out(self, q, out):

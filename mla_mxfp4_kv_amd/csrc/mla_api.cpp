@@ -307,4 +307,16 @@ int mla_decode_bf16(const void* q, const void* kv_bf16, const int32_t* kv_indptr
   return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, nullptr, kv_indptr, out, sm_scale, workspace, stream);
 }
 
+int mla_decode_fp8_paged(const void* q, const void* kv_fp8, const float* kv_scale, const int32_t* kv_indices,
+                         const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
+  return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, kv_indices, kv_indptr, out, sm_scale, workspace,
+                       stream, true);
+}
+
+int mla_decode_bf16_paged(const void* q, const void* kv_bf16, const int32_t* kv_indices,
+                          const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
+  return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, kv_indices, kv_indptr, out, sm_scale, workspace,
+                       stream, true);
+}
+
 }  // extern "C"

@@ -183,6 +183,63 @@ __device__ __forceinline__ void lds_tr_x8(uint32_t addr, i32x2_t (&v)[8]) {
   }
 }
 
+// ---- per-token row lists (kv_indices, page size 1) ----------------------
+// A wave keeps the row indices of four tiles in a ring of 128-byte slots
+// after the tile buffers: the indices of tile i + 3 are loaded while tile
+// i is computed, so those of tile i + 1 have landed when its rows are
+// staged.
+constexpr int kIdxSlot = 128;
+constexpr int kIdxWave = 4 * kIdxSlot;
+constexpr int kLdsGather = kLdsTotal + kWaves * kIdxWave;
+static_assert(kLdsGather <= 160 * 1024, "LDS budget of one gfx950 CU");
+
+// kv_indices[t0 .. t0 + kTile - 1] (the last valid one repeated past the
+// item's end) into `slot`, one 4-byte direct load per lane.
+template <bool kFp8>
+__device__ __forceinline__ void stage_idx(uint8_t* slot, const int32_t* __restrict__ kv_indices, int t0,
+                                          int nvalid, int lane) {
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  if (lane < Cfg<kFp8>::kTile) {
+    const int r = min(lane, nvalid - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(kv_indices + t0 + r), (MLA_LDS void*)slot, 4, 0, 0);
+  }
+}
+
+// Stage the tile whose row indices sit in `slot`: lane chunk c = 64*i + lane
+// of instruction i is 16-byte chunk c % (row/16) of tile row c / (row/16)
+// (rows past the item's end repeat the last valid row's last chunk). Lane r
+// reads index r once; the DMA lanes take theirs by cross-lane permute, so
+// the only LDS read is waited for inside its own block.
+template <bool kFp8>
+__device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __restrict__ kv, const uint8_t* slot,
+                                             int nvalid, int lane) {
+  using C = Cfg<kFp8>;
+  constexpr int kCpr = C::kRow / 16;
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const int last = min(nvalid, C::kTile) - 1;
+  uint32_t my;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(my)
+               : "v"(lds_addr(slot) + 4u * (uint32_t)min(lane, C::kTile - 1)));
+  uint32_t off[kDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int c = 64 * i + lane;
+    int r = c / kCpr;
+    int w = c - kCpr * r;
+    if (r > last) {
+      r = last;
+      w = kCpr - 1;
+    }
+    const uint32_t phys = (uint32_t)__shfl((int)my, r);
+    off[i] = phys * (uint32_t)C::kRow + 16u * (uint32_t)w;
+  }
+#pragma unroll
+  for (int i = 0; i < kDma; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(kv + off[i]), (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+}
+
 __device__ __forceinline__ float max_over_groups(float v) {
   // max over lanes h, h+16, h+32, h+48 (the 4 lane groups of head h); the
   // swap results are copied to scalars before their bit casts
@@ -411,14 +468,15 @@ __device__ __forceinline__ void pv_bf16(const uint8_t* buf, const bf16x4_t& pa, 
   pv_bf16_group<3>(ta, pa, o);
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kGather>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                         const float* __restrict__ kv_scale, const int32_t* __restrict__ kv_indptr,
-                        uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
-                        float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
+                        const int32_t* __restrict__ kv_indices, uint16_t* __restrict__ out,
+                        const int32_t* __restrict__ plan, float* __restrict__ part_lse,
+                        float* __restrict__ part_out, float csc) {
   using C = Cfg<kFp8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kGather ? kLdsGather : kLdsTotal];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -526,17 +584,46 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
           pv_bf16(buf, pa, o, lane);
         }
       };
-      if (ntiles > 0) stage_tile<kFp8>(ring, kv, t_first, ke - t_first, lane);
-      for (int i = 0; i < ntiles; ++i) {
-        // tile i + 1 goes into the other buffer before tile i is waited for
-        if (i + 1 < ntiles) {
-          const int tn = t_first + (i + 1) * C::kStride;
-          stage_tile<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv, tn, ke - tn, lane);
-          wait_vm<kDma>();
-        } else {
+      if constexpr (kGather) {
+        // Per iteration the wave issues the rows of tile i + 1 (18 loads)
+        // and the indices of tile i + 3 (1 load; past the item's last tile
+        // they repeat its indices, so the counts below never change).
+        uint8_t* islot = lds + kLdsTotal + wave * kIdxWave;
+        auto tile_t0 = [&](int k) { return t_first + min(k, ntiles - 1) * C::kStride; };
+        if (ntiles > 0) {
+          stage_idx<kFp8>(islot, kv_indices, tile_t0(0), ke - tile_t0(0), lane);
+          stage_idx<kFp8>(islot + kIdxSlot, kv_indices, tile_t0(1), ke - tile_t0(1), lane);
           wait_vm<0>();
+          stage_gather<kFp8>(ring, kv, islot, ke - t_first, lane);
+          stage_idx<kFp8>(islot + 2 * kIdxSlot, kv_indices, tile_t0(2), ke - tile_t0(2), lane);
         }
-        compute(ring + (i & 1) * kTileBytes, i);
+        for (int i = 0; i < ntiles; ++i) {
+          if (i + 1 < ntiles) {
+            wait_vm<kDma + 1>();   // indices of tile i + 1 (then: rows of i, indices of i + 2)
+            const int tn = t_first + (i + 1) * C::kStride;
+            stage_gather<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv, islot + ((i + 1) & 3) * kIdxSlot, ke - tn,
+                               lane);
+            stage_idx<kFp8>(islot + ((i + 3) & 3) * kIdxSlot, kv_indices, tile_t0(i + 3), ke - tile_t0(i + 3),
+                            lane);
+            wait_vm<kDma + 2>();   // rows of tile i (then: indices of i + 2, rows of i + 1, indices of i + 3)
+          } else {
+            wait_vm<0>();
+          }
+          compute(ring + (i & 1) * kTileBytes, i);
+        }
+      } else {
+        if (ntiles > 0) stage_tile<kFp8>(ring, kv, t_first, ke - t_first, lane);
+        for (int i = 0; i < ntiles; ++i) {
+          // tile i + 1 goes into the other buffer before tile i is waited for
+          if (i + 1 < ntiles) {
+            const int tn = t_first + (i + 1) * C::kStride;
+            stage_tile<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv, tn, ke - tn, lane);
+            wait_vm<kDma>();
+          } else {
+            wait_vm<0>();
+          }
+          compute(ring + (i & 1) * kTileBytes, i);
+        }
       }
 
       // ---- merge the 4 waves' states ----
@@ -605,18 +692,24 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
 
 }  // namespace
 
-size_t decode_dense_lds_bytes() { return (size_t)kLdsTotal; }
+size_t decode_dense_lds_bytes() { return (size_t)kLdsGather; }
+
+template <bool kFp8, bool kGather>
+static void launch_dense(const DecodeArgs& a, const float* kv_scale, void* stream) {
+  hipLaunchKernelGGL((mla_decode_dense_kernel<kFp8, kGather>), dim3(a.grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, (const uint16_t*)a.q, a.kv_packed, kv_scale, a.kv_indptr, a.kv_indices,
+                     (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+}
 
 int launch_decode_dense(const DecodeArgs& a, bool fp8, const float* kv_scale, void* stream) {
   if (a.num_slots <= 0 || a.grid <= 0) return (int)hipSuccess;
+  const bool gather = a.kv_indices != nullptr;
   if (fp8) {
-    hipLaunchKernelGGL(mla_decode_dense_kernel<true>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const uint16_t*)a.q, a.kv_packed, kv_scale, a.kv_indptr, (uint16_t*)a.out, a.plan,
-                       a.part_lse, a.part_out, a.score_scale_log2);
+    if (gather) launch_dense<true, true>(a, kv_scale, stream);
+    else launch_dense<true, false>(a, kv_scale, stream);
   } else {
-    hipLaunchKernelGGL(mla_decode_dense_kernel<false>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const uint16_t*)a.q, a.kv_packed, kv_scale, a.kv_indptr, (uint16_t*)a.out, a.plan,
-                       a.part_lse, a.part_out, a.score_scale_log2);
+    if (gather) launch_dense<false, true>(a, kv_scale, stream);
+    else launch_dense<false, false>(a, kv_scale, stream);
   }
   return (int)hipGetLastError();
 }

@@ -1,6 +1,6 @@
-"""GPU parity of the MXFP4 decode over per-token row lists
-(mla_decode_mxfp4_paged, page size 1) against the fp64 oracle, through the
-C ABI. Same bar as the contiguous decode."""
+"""GPU parity of the decodes over per-token row lists (mla_decode_mxfp4_paged,
+mla_decode_fp8_paged, mla_decode_bf16_paged; page size 1) against the fp64
+oracle, through the C ABI. Same bar as the contiguous decodes."""
 
 import math
 import sys
@@ -10,6 +10,7 @@ import pytest
 import torch
 
 from mla_mxfp4_kv_amd import binding, synth
+from oracle import dense_ref as dref
 from oracle import mxfp4_ref as ref
 
 pytestmark = pytest.mark.gpu
@@ -171,4 +172,97 @@ def test_gather_workload_b256_page_shuffled():
         lo, hi = int(ind[b]), int(ind[b + 1])
         want = ref.mla_decode_ref_seq(qb[b], packed[lo:hi].cpu().numpy(), scales[lo:hi].cpu().numpy(), w.sm_scale)
         _check(got[b], want, f"b256 gather b={b}")
+    assert np.all(np.isfinite(got))
+
+
+def _dense_case(fmt, lens, seed, extra=2.0):
+    w = synth.Workload("g", len(lens), None, None, 1.0, False, seed)
+    q, cache, scale, indptr, _ = synth.make_dense_inputs(w, fmt, lengths=lens)
+    t = int(indptr[-1])
+    rng = np.random.default_rng(seed)
+    rows = max(1, int(extra * t))
+    pos = torch.from_numpy(rng.permutation(rows)[:t].astype(np.int32))
+    if fmt == "fp8":
+        pool = torch.from_numpy(rng.integers(0, 0x7E, (rows, 576), dtype=np.uint8))
+    else:
+        pool = torch.randn(rows, 576, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    pool[pos.long()] = cache
+    return q, cache, scale, indptr, pool, pos
+
+
+def _dense_oracle(fmt, q, pool, scale, pos, indptr):
+    qb = _qbits(q)
+    rows = pool.numpy() if fmt == "fp8" else pool.view(torch.int16).numpy().view(np.uint16)
+    out = np.zeros((len(indptr) - 1, 16, 512))
+    for b in range(len(indptr) - 1):
+        sel = pos.numpy()[int(indptr[b]):int(indptr[b + 1])]
+        if fmt == "fp8":
+            out[b] = dref.mla_decode_ref_fp8_seq(qb[b], rows[sel], float(scale[0]), SM)
+        else:
+            out[b] = dref.mla_decode_ref_bf16_seq(qb[b], rows[sel], SM)
+    return out
+
+
+def _dense_paged(dec, fmt, q, pool, scale, pos):
+    if fmt == "fp8":
+        return dec.fp8_paged(q.cuda(), pool.cuda(), scale.cuda(), pos.cuda(), sm_scale=SM)
+    return dec.bf16_paged(q.cuda(), pool.cuda(), pos.cuda(), sm_scale=SM)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+@pytest.mark.parametrize("lens,num_cus", CASES)
+def test_dense_gather_matches_oracle(fmt, lens, num_cus):
+    _say(f"case {fmt} gather lens={lens} num_cus={num_cus}")
+    q, cache, scale, indptr, pool, pos = _dense_case(fmt, lens, seed=sum(lens) + 7)
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=num_cus)
+    out = _dense_paged(dec, fmt, q, pool, scale, pos)
+    torch.cuda.synchronize()
+    _check(out.float().cpu().numpy(), _dense_oracle(fmt, q, pool, scale, pos, indptr.numpy()),
+           f"{fmt} gather {lens}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+def test_dense_identity_rows_are_bit_identical(fmt):
+    _say(f"case {fmt} gather identity")
+    lens = [700, 33, 4100, 1]
+    w = synth.Workload("g", len(lens), None, None, 1.0, False, 19)
+    q, cache, scale, indptr, _ = synth.make_dense_inputs(w, fmt, lengths=lens)
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=9)
+    ident = torch.arange(int(indptr[-1]), dtype=torch.int32)
+    if fmt == "fp8":
+        a = dec.fp8(q.cuda(), cache.cuda(), scale.cuda(), sm_scale=SM).clone()
+    else:
+        a = dec.bf16(q.cuda(), cache.cuda(), sm_scale=SM).clone()
+    b = _dense_paged(dec, fmt, q, cache, scale, ident)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+def test_dense_gather_workload_b256_page_shuffled(fmt):
+    w = synth.WORKLOADS["b256_kv8192"]
+    _say(f"case {fmt} gather b256_kv8192: generating")
+    q, cache, scale, indptr, lens = synth.make_dense_inputs(w, fmt, device="cuda")
+    t = int(indptr[-1])
+    g = torch.Generator(device="cpu").manual_seed(98)
+    perm = torch.randperm(t // 16, generator=g).to(torch.int32)
+    idx = (perm.repeat_interleave(16) * 16 + torch.arange(16, dtype=torch.int32).repeat(t // 16)).cuda()
+    pool = torch.empty_like(cache)
+    pool[idx.long()] = cache
+    dec = binding.MlaDecode(indptr.tolist(), device="cuda")
+    _say(f"case {fmt} gather b256_kv8192: decode")
+    out = dec.fp8_paged(q, pool, scale, idx, sm_scale=w.sm_scale) if fmt == "fp8" else \
+        dec.bf16_paged(q, pool, idx, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    qb = _qbits(q)
+    ind = indptr.numpy()
+    for b in (0, 131, 255):
+        lo, hi = int(ind[b]), int(ind[b + 1])
+        if fmt == "fp8":
+            want = dref.mla_decode_ref_fp8_seq(qb[b], cache[lo:hi].cpu().numpy(), float(scale[0]), w.sm_scale)
+        else:
+            want = dref.mla_decode_ref_bf16_seq(
+                qb[b], cache[lo:hi].cpu().contiguous().view(torch.int16).numpy().view(np.uint16), w.sm_scale)
+        _check(got[b], want, f"{fmt} b256 gather b={b}")
     assert np.all(np.isfinite(got))
