@@ -30,8 +30,10 @@ KERNEL_SRC = {
     "fp8": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
     "bf16": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
 }
-KERNEL_NAME = {"mxfp4": "mla_decode_kernel<false>", "fp8": "mla_decode_dense_kernel<true>",
-               "bf16": "mla_decode_dense_kernel<false>"}
+KERNEL_NAME = {"mxfp4": "mla_decode_kernel<false>", "fp8": "mla_decode_dense_kernel<true, false>",
+               "bf16": "mla_decode_dense_kernel<false, false>"}
+GATHER_KERNEL_NAME = {"mxfp4": "mla_decode_kernel<true>", "fp8": "mla_decode_dense_kernel<true, true>",
+                      "bf16": "mla_decode_dense_kernel<false, true>"}
 
 
 def kernel_source_hash(fmt: str = "mxfp4") -> str:
@@ -147,8 +149,8 @@ def main(argv=None):
     ap.add_argument("--kv-format", default="mxfp4", choices=["mxfp4", "fp8", "bf16"],
                     help="cache format: the MXFP4 headline path, or the fp8 / bf16 sibling decodes")
     ap.add_argument("--gather", type=int, default=0, metavar="PAGE",
-                    help="MXFP4 only: scatter the rows over the pool in pages of PAGE rows (seeded "
-                         "shuffle) and decode through per-token kv_indices (mla_decode_mxfp4_paged)")
+                    help="scatter the rows over the pool in pages of PAGE rows (seeded shuffle) and "
+                         "decode through per-token kv_indices (the *_paged entry points)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
@@ -188,9 +190,6 @@ def main(argv=None):
     out = torch.empty(w.batch, 16, 512, dtype=torch.bfloat16, device=dev)
     kv_indices = None
     if args.gather:
-        if fmt != "mxfp4":
-            print("--gather is built for the MXFP4 decode only", file=sys.stderr)
-            return 2
         page = args.gather
         if total % page:
             print(f"--gather {page}: the token count {total} is not a multiple of the page", file=sys.stderr)
@@ -200,16 +199,25 @@ def main(argv=None):
         kv_indices = (perm.repeat_interleave(page) * page
                       + torch.arange(page, dtype=torch.int32).repeat(total // page)).to(dev)
         pool_p = torch.empty_like(packed)
-        pool_s = torch.empty_like(scales)
         pool_p[kv_indices.long()] = packed
-        pool_s[kv_indices.long()] = scales
-        packed, scales = pool_p, pool_s
-        binding.check_kv_indices(kv_indices, indptr.tolist(), packed.shape[0])
+        if fmt == "mxfp4":
+            pool_s = torch.empty_like(scales)
+            pool_s[kv_indices.long()] = scales
+            scales = pool_s
+        packed = pool_p
+        binding.check_kv_indices(kv_indices, indptr.tolist(), packed.shape[0],
+                                 packed.shape[1] * packed.element_size())
         torch.cuda.synchronize()
-    if kv_indices is not None:
+    if kv_indices is not None and fmt == "mxfp4":
         def call():
             binding.decode_mxfp4_paged(q, packed, scales, kv_indices, dec.kv_indptr, out, w.sm_scale,
                                        dec.workspace)
+    elif kv_indices is not None and fmt == "fp8":
+        def call():
+            binding.decode_fp8_paged(q, packed, scales, kv_indices, dec.kv_indptr, out, w.sm_scale, dec.workspace)
+    elif kv_indices is not None:
+        def call():
+            binding.decode_bf16_paged(q, packed, kv_indices, dec.kv_indptr, out, w.sm_scale, dec.workspace)
     elif fmt == "mxfp4":
         def call():
             dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
@@ -323,7 +331,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if args.gather else measured_traffic(w.name, fmt),
-            "kernel": "mla_decode_kernel<true>" if args.gather else KERNEL_NAME[fmt],
+            "kernel": GATHER_KERNEL_NAME[fmt] if args.gather else KERNEL_NAME[fmt],
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_source_sha256": kernel_source_hash(fmt),
