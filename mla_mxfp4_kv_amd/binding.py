@@ -352,6 +352,23 @@ class MlaDecodeDevicePlan:
         decode(q, kv_packed, kv_scale, kv_indptr, out, sm_scale, self.workspace, stream)
         return out
 
+    def decode_paged(self, fmt, q, pool, kv_scale, kv_indices, kv_indptr, out,
+                     sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        """Row-list decode on the device plan: fmt "mxfp4" (pool = packed rows,
+        kv_scale = E8M0 rows), "fp8" (kv_scale = float32 [1]) or "bf16"
+        (kv_scale unused). The indices are not checked (they may change on
+        the device between graph replays): the caller keeps them in range."""
+        _validate_qo(q, out, self.batch)
+        if fmt == "mxfp4":
+            decode_mxfp4_paged(q, pool, kv_scale, kv_indices, kv_indptr, out, sm_scale, self.workspace, stream)
+        elif fmt == "fp8":
+            decode_fp8_paged(q, pool, kv_scale, kv_indices, kv_indptr, out, sm_scale, self.workspace, stream)
+        elif fmt == "bf16":
+            decode_bf16_paged(q, pool, kv_indices, kv_indptr, out, sm_scale, self.workspace, stream)
+        else:
+            raise ValueError(f"unknown cache format {fmt!r}")
+        return out
+
     def decode_fp8(self, q, kv_fp8, kv_scale, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0),
                    stream=None):
         """fp8-cache decode on the device plan (kv_fp8 uint8 [T,576], kv_scale float32 [1])."""

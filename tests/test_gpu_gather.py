@@ -266,3 +266,69 @@ def test_dense_gather_workload_b256_page_shuffled(fmt):
                 qb[b], cache[lo:hi].cpu().contiguous().view(torch.int16).numpy().view(np.uint16), w.sm_scale)
         _check(got[b], want, f"{fmt} b256 gather b={b}")
     assert np.all(np.isfinite(got))
+
+
+def test_graph_replay_device_plan_with_row_lists():
+    """GPU-side plan + the three row-list decodes recorded in one HIP graph;
+    between replays both the offsets and the row indices change in place on
+    the device (a serving step: tokens appended, pages remapped)."""
+    steps = [[37, 1025, 0, 300], [38, 1026, 1, 301], [200, 64, 900, 5]]
+    batch = 4
+    max_total = max(sum(st) for st in steps)
+    pool_rows = 3 * max_total
+    rng = np.random.default_rng(61)
+    qb = torch.randn(batch, 16, 576, generator=torch.Generator().manual_seed(62)).to(torch.bfloat16)
+    pool_p = torch.from_numpy(rng.integers(0, 256, (pool_rows, 288), dtype=np.uint8))
+    # scales 2^-5 .. 2^0 keep the decoded rows in the range of the synthetic
+    # workloads (random bytes with larger scales make outputs that cancel
+    # between values in the hundreds, below what a bf16 P can resolve)
+    pool_s = torch.from_numpy(rng.integers(122, 128, (pool_rows, 18), dtype=np.uint8))
+    pool_8 = torch.from_numpy(rng.integers(0, 0x7E, (pool_rows, 576), dtype=np.uint8))
+    pool_16 = torch.randn(pool_rows, 576, generator=torch.Generator().manual_seed(63)).to(torch.bfloat16)
+    scale8 = torch.tensor([0.0173], dtype=torch.float32)
+    dev = [t.cuda() for t in (qb, pool_p, pool_s, pool_8, pool_16, scale8)]
+    qd, pd, sd, p8, p16, s8 = dev
+    dp = binding.MlaDecodeDevicePlan(batch, max_total, num_cus=6)
+    kvi = torch.zeros(batch + 1, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(max_total, dtype=torch.int32, device="cuda")
+    outs = [torch.empty(batch, 16, 512, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    stream = torch.cuda.Stream()
+
+    def record():
+        dp.plan(kvi, stream=stream)
+        dp.decode_paged("mxfp4", qd, pd, sd, idx, kvi, outs[0], sm_scale=SM, stream=stream)
+        dp.decode_paged("fp8", qd, p8, s8, idx, kvi, outs[1], sm_scale=SM, stream=stream)
+        dp.decode_paged("bf16", qd, p16, None, idx, kvi, outs[2], sm_scale=SM, stream=stream)
+
+    with torch.cuda.stream(stream):
+        record()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        record()
+    torch.cuda.synchronize()
+    qbits = _qbits(qb)
+    for k, lens in enumerate(steps):
+        ind = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        rows = rng.choice(pool_rows, size=int(ind[-1]), replace=False).astype(np.int32)
+        _say(f"replay step {k} lens={lens}")
+        kvi.copy_(torch.from_numpy(ind.astype(np.int32)))
+        idx.zero_()
+        idx[: len(rows)].copy_(torch.from_numpy(rows))
+        torch.cuda.synchronize()
+        want_mx = ref.mla_decode_ref_gather(qbits, pool_p.numpy(), pool_s.numpy(), rows, ind, SM)
+        want_8 = np.zeros_like(want_mx)
+        want_16 = np.zeros_like(want_mx)
+        b16 = pool_16.view(torch.int16).numpy().view(np.uint16)
+        for b in range(batch):
+            sel = rows[ind[b]:ind[b + 1]]
+            want_8[b] = dref.mla_decode_ref_fp8_seq(qbits[b], pool_8.numpy()[sel], float(scale8[0]), SM)
+            want_16[b] = dref.mla_decode_ref_bf16_seq(qbits[b], b16[sel], SM)
+        for rep in range(2):
+            for o in outs:
+                o.fill_(7)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for name, o, want in (("mxfp4", outs[0], want_mx), ("fp8", outs[1], want_8), ("bf16", outs[2], want_16)):
+                _check(o.float().cpu().numpy(), want, f"{name} step {k} replay {rep}")
