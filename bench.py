@@ -68,14 +68,30 @@ def measured_traffic(workload: str, fmt: str = "mxfp4"):
 
 def copy_probe(nbytes: int, reps: int) -> int:
     """Plain device-to-device copy of a known size (calibrates the
-    FETCH_SIZE / WRITE_SIZE counters against bytes actually moved)."""
+    FETCH_SIZE / WRITE_SIZE counters against bytes actually moved) and a
+    read-only pass over it, each timed with HIP events: the bandwidth a
+    plain copy / read reaches on this machine."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
+    dst.copy_(src)
+    words = src.view(torch.int64)
+    words.sum()
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
     for _ in range(reps):
         dst.copy_(src)
+    e1.record()
+    for _ in range(reps):
+        words.sum()
+    e2.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+    copy_s = e0.elapsed_time(e1) * 1e-3 / reps
+    read_s = e1.elapsed_time(e2) * 1e-3 / reps
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps,
+                      "copy_gbs_read_plus_write": round(2 * nbytes / copy_s / 1e9, 1),
+                      "read_gbs": round(nbytes / read_s / 1e9, 1)}), flush=True)
     return 0
 QO_BYTES_PER_SEQ = 16 * 576 * 2 + 16 * 512 * 2
 PARTIAL_BYTES = 16 * (512 + 1) * 4
