@@ -31,6 +31,8 @@
 //  * The 4 waves' (m, l, O) merge through LDS; a whole-sequence item writes
 //    bf16 output, any other item a normalised fp32 partial and its base-2
 //    LSE, which the MXFP4 library's reduce kernel merges.
+//  * kGather: rows listed per token (kv_indices, page size 1); each wave
+//    keeps the row indices of the next three tiles in an LDS ring.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

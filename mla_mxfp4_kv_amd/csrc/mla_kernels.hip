@@ -37,6 +37,10 @@
 //  * The 4 pairs' (m, l, O) are merged through LDS; a whole-sequence item
 //    writes bf16 output directly, any other item writes a normalised fp32
 //    partial and its base-2 LSE for the reduce kernel.
+//  * kGather: the same kernel over a cache whose rows are listed per token
+//    (kv_indices, page size 1, as the 676098 page passes its decode): the
+//    scorer stages each tile's row indices a round ahead and the tile's rows
+//    and per-row scale chunks are gathered through them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -792,11 +796,14 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 }
 
 // LSE-weighted merge of the partials of one sequence (or zero fill of an
-// empty one), for plans with long splits (many partials per sequence): out = sum_p 2^(lse_p - M) O_p / sum_p 2^(lse_p - M) with
-// M = max_p lse_p over non-empty partials. One workgroup per (reduce entry,
-// head, quarter of the 512 dims); its 16 waves take every 16th partial (so
-// a long split sequence is merged by many waves with their loads in flight)
-// and are summed through LDS. Lane covers 2 consecutive output dims.
+// empty one), for plans with long splits (many partials per sequence):
+// out = sum_p 2^(lse_p - M) O_p / sum_p 2^(lse_p - M) with M = max_p lse_p
+// over non-empty partials (each wave uses its own running max, the waves'
+// sums are rescaled to the common one when merged). One workgroup per
+// (reduce entry, head, quarter of the 512 dims); its 16 waves take every
+// 16th partial (so a long split sequence is merged by many waves with their
+// loads in flight) and are summed through LDS. Lane covers 2 consecutive
+// output dims.
 constexpr int kReduceWaves = 16;
 constexpr int kReduceThreads = 64 * kReduceWaves;
 constexpr int kReduceSplit = 4;                      // dim quarters per head
@@ -823,50 +830,53 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
     if (wave == 0) *dst = 0u;
     return;
   }
-  // pass 1: M over non-empty partials
+  // One pass: each wave keeps a running max over its partials (every 16th,
+  // eight loads in flight) and rescales its sums when the max rises; the 16
+  // waves' (max, sums) are then merged through LDS.
+  constexpr int kUnroll = 8;
   float m = kNegInf;
-  for (int i = threadIdx.x; i < cnt; i += kReduceThreads) {
-    const float v = part_lse[(size_t)(first + i) * kHeads + h];
-    if (v != kNegInf) m = fmaxf(m, v);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) max_s[wave] = m;
-  __syncthreads();
-  m = max_s[0];
-#pragma unroll
-  for (int w = 1; w < kReduceWaves; ++w) m = fmaxf(m, max_s[w]);
-  // pass 2: this wave's partials
   f32x2_t acc = {0.f, 0.f};
   float wsum = 0.f;
-  for (int i0 = wave; i0 < cnt; i0 += 4 * kReduceWaves) {
-    float v[4];
-    f32x2_t o[4];
+  for (int i0 = wave; i0 < cnt; i0 += kUnroll * kReduceWaves) {
+    float v[kUnroll];
+    f32x2_t o[kUnroll];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kUnroll; ++u) {
       const int i = min(i0 + u * kReduceWaves, cnt - 1);
       v[u] = part_lse[(size_t)(first + i) * kHeads + h];
       o[u] = *(const f32x2_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + d);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kUnroll; ++u) {
       if (i0 + u * kReduceWaves < cnt && v[u] != kNegInf) {
-        const float w = __builtin_amdgcn_exp2f(v[u] - m);
-        wsum += w;
-        acc += w * o[u];
+        const float m_new = fmaxf(m, v[u]);
+        const float keep = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
+        const float w = __builtin_amdgcn_exp2f(v[u] - m_new);
+        wsum = wsum * keep + w;
+        acc = acc * keep + w * o[u];
+        m = m_new;
       }
     }
   }
   acc_s[wave][lane] = acc;
-  if (lane == 0) wsum_s[wave] = wsum;
+  if (lane == 0) {
+    wsum_s[wave] = wsum;
+    max_s[wave] = m;
+  }
   __syncthreads();
   if (wave == 0) {
-    f32x2_t tot = acc_s[0][lane];
-    float ws = wsum_s[0];
+    float mm = kNegInf;
 #pragma unroll
-    for (int w = 1; w < kReduceWaves; ++w) {
-      tot += acc_s[w][lane];
-      ws += wsum_s[w];
+    for (int w = 0; w < kReduceWaves; ++w) mm = fmaxf(mm, max_s[w]);
+    f32x2_t tot = {0.f, 0.f};
+    float ws = 0.f;
+#pragma unroll
+    for (int w = 0; w < kReduceWaves; ++w) {
+      if (max_s[w] != kNegInf) {
+        const float sc = __builtin_amdgcn_exp2f(max_s[w] - mm);
+        tot += sc * acc_s[w][lane];
+        ws += sc * wsum_s[w];
+      }
     }
     const float inv = ws != 0.f ? 1.0f / ws : 0.f;
     *dst = pack2(tot[0] * inv, tot[1] * inv);
