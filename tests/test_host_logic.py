@@ -1,0 +1,81 @@
+"""CPU checks of the host-side helpers around the decode: the index guard of
+the row-list decodes, the benchmark's byte accounting and the cache byte
+counts of the three formats (no GPU)."""
+
+import os
+import sys
+
+import pytest
+import torch
+
+from mla_mxfp4_kv_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def test_kv_bytes_per_format():
+    assert synth.kv_bytes(1) == 288 + 18
+    assert synth.kv_bytes(10, "fp8") == 5760
+    assert synth.kv_bytes(10, "bf16") == 11520
+    # the headline cache sizes quoted in the benchmark and the design notes
+    assert synth.kv_bytes(256 * 8192) == 641728512
+    assert synth.kv_bytes(256 * 8192, "fp8") == 1207959552
+    assert synth.kv_bytes(256 * 8192, "bf16") == 2415919104
+
+
+def test_algorithmic_bytes():
+    import bench
+    words = [0] * 16
+    words[2] = 256          # batch
+    words[9] = 0            # partials
+    assert bench.algorithmic_bytes(words, 256 * 8192) == 650641408
+    assert bench.algorithmic_bytes(words, 256 * 8192, "fp8") == 1216872448
+    assert bench.algorithmic_bytes(words, 256 * 8192, gather=True) == 650641408 + 4 * 256 * 8192
+    words[9] = 3            # each partial written once and read once
+    assert bench.algorithmic_bytes(words, 0) - bench.algorithmic_bytes([0] * 16, 0) == \
+        256 * bench.QO_BYTES_PER_SEQ + 2 * 3 * 16 * 513 * 4
+
+
+def test_check_kv_indices():
+    ind = [3, 5, 9]                      # tokens 3..8 are read
+    idx = torch.arange(12, dtype=torch.int32)
+    binding.check_kv_indices(idx, ind, pool_rows=12)
+    # entries before kv_indptr[0] are not read, so they may hold anything
+    bad_head = idx.clone()
+    bad_head[0] = -7
+    binding.check_kv_indices(bad_head, ind, pool_rows=12)
+    with pytest.raises(ValueError):
+        binding.check_kv_indices(idx, ind, pool_rows=8)              # row 8 outside a pool of 8
+    with pytest.raises(ValueError):
+        neg = idx.clone()
+        neg[4] = -1
+        binding.check_kv_indices(neg, ind, pool_rows=12)
+    with pytest.raises(ValueError):
+        binding.check_kv_indices(idx[:8], ind, pool_rows=12)         # shorter than kv_indptr[-1]
+    with pytest.raises(ValueError):
+        binding.check_kv_indices(idx.to(torch.int64), ind, pool_rows=12)
+    with pytest.raises(ValueError):
+        binding.check_kv_indices(idx, ind, pool_rows=2 ** 32 // 288 + 1)  # 32-bit row offsets
+    binding.check_kv_indices(idx, ind, pool_rows=2 ** 32 // 288)          # the largest pool that fits
+    binding.check_kv_indices(idx, [0, 0], pool_rows=1)               # nothing read
+
+
+def test_fp8_quantiser_edge_cases():
+    zeros = torch.zeros(3, 576, dtype=torch.bfloat16)
+    codes, scale = synth.quantize_fp8_per_tensor(zeros)
+    assert float(scale) == 1.0 and int(codes.max()) == 0
+    x = torch.full((2, 576), -2.5, dtype=torch.bfloat16)
+    codes, scale = synth.quantize_fp8_per_tensor(x)
+    assert torch.all(codes == 0xFE)                                  # -448 after scaling
+
+
+def test_dense_inputs_share_the_mxfp4_draws():
+    w = synth.Workload("t", 2, None, None, 1.0, False, 5)
+    q, _, _, ind, _ = synth.make_inputs(w, lengths=[3, 4])
+    q2, lat, scale, ind2, _ = synth.make_dense_inputs(w, "bf16", lengths=[3, 4])
+    assert torch.equal(q, q2) and torch.equal(ind, ind2) and scale is None
+    assert lat.shape == (7, 576) and lat.dtype == torch.bfloat16
+    with pytest.raises(ValueError):
+        synth.make_dense_inputs(w, "fp4", lengths=[3, 4])
