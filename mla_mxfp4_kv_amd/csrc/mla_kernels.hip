@@ -85,6 +85,12 @@ constexpr int kMergeFrag = kPairs * 32 * 64 * 16;   // O fragments: [pair][fragm
 constexpr int kMergeBytes = kMergeFrag + kPairs * 2 * kHeads * 4;
 constexpr int kLdsTotal = (kLdsMain > kMergeBytes) ? kLdsMain : kMergeBytes;
 constexpr float kTau = 8.0f;                    // lazy-rescale threshold (base-2 units)
+// Cache policy of the tile loads: non-temporal (nt). The cache is read once
+// per call, and marking the stream non-temporal measured 6% faster for this
+// kernel and 12% for the fp8/bf16 ones at B=256, kv=8192 (same process,
+// interleaved) than the default policy; the scope bits (sc0/sc1) changed
+// nothing.
+constexpr int kStream = 2;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMInit = -1.0e30f;              // running max before the first tile (finite: no inf - inf)
 
@@ -146,20 +152,20 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
 #pragma unroll
     for (int i = kFirst; i < kFirst + kCount; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(kv_t + 1024 * i + lane_off),
-                                       (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+                                       (MLA_LDS void*)(buf + 1024 * i), 16, 0, kStream);
   } else {
     const uint32_t last = (uint32_t)(nvalid * kRowBytes - 16);
 #pragma unroll
     for (int i = kFirst; i < kFirst + kCount; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(kv_t + min(1024 * i + lane_off, last)),
-                                       (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+                                       (MLA_LDS void*)(buf + 1024 * i), 16, 0, kStream);
   }
   if constexpr (kScales) {
     const uintptr_t first = (uintptr_t)(sc + (size_t)t0 * kBlocks);
     const uintptr_t last_chunk = (first + (uintptr_t)(kBlocks * min(nvalid, kTile)) - 1) & ~(uintptr_t)15;
     const uintptr_t src = min((first & ~(uintptr_t)15) + lane_off, last_chunk);
     if (lane < kRawChunks)
-      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(buf + kLdsRaw), 16, 0, kStream);
   }
 }
 
@@ -211,9 +217,9 @@ __device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __rest
   const uintptr_t srow = (uintptr_t)(sc + (size_t)(uint32_t)idx[min(lane >> 1, last)] * kBlocks);
 #pragma unroll
   for (int i = 0; i < kRowDma; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(kv + off[i]), (MLA_LDS void*)(buf + 1024 * i), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(kv + off[i]), (MLA_LDS void*)(buf + 1024 * i), 16, 0, kStream);
   __builtin_amdgcn_global_load_lds((const void*)((srow & ~(uintptr_t)15) + 16 * (uintptr_t)(lane & 1)),
-                                   (MLA_LDS void*)(buf + kLdsRaw), 16, 0, 0);
+                                   (MLA_LDS void*)(buf + kLdsRaw), 16, 0, kStream);
 }
 
 // LDS address of the scale bytes of tile row `row`. delta: in the
