@@ -217,6 +217,38 @@ int mla_decode_bf16_paged(const void* q, const void* kv_bf16, const int32_t* kv_
                           const int32_t* kv_indptr, void* out, float sm_scale,
                           void* workspace, void* stream);
 
+/* The three decodes over a page table (page "kernelbot-amd-mixed-mla-676098",
+ * _aiter_mla_decode, passes kv_indptr, kv_indices, kv_last_page_len and
+ * page_size to its decode; page_size is 1 there). Sequence b owns pages
+ * page_indices[page_indptr[b] .. page_indptr[b+1]-1] (int32, device, 4-byte
+ * aligned, both), each a run of page_size consecutive rows of the row pools
+ * (MXFP4: kv_packed [R, 288] and kv_scale [R, 18], 2-byte aligned; fp8:
+ * uint8 [R, 576]; bf16: bfloat16 [R, 576]). Token t of the sequence (t from
+ * 0) is pool row page_indices[page_indptr[b] + t / page_size] * page_size +
+ * t % page_size. kv_indptr is the device copy of the token offsets the plan
+ * was built from: sequence b has kv_indptr[b+1] - kv_indptr[b] tokens, that
+ * is (pages - 1) * page_size plus the valid rows of its last page
+ * (kv_last_page_len, 1..page_size). page_size >= 1 (any value; page_size 1
+ * with page_indptr = kv_indptr is the row list of the *_paged calls).
+ * The caller guarantees that the page counts match the token counts and
+ * that every row read lies in [0, R) with R * row bytes below 2^32 (the
+ * Python binding checks both); the library cannot check them without
+ * reading the arrays. Errors: those of the *_paged calls, plus
+ * MLA_ERR_INVALID for page_size < 1 or a null or misaligned page_indptr
+ * or page_indices. */
+int mla_decode_mxfp4_page_table(const void* q, const void* kv_packed, const void* kv_scale,
+                                const int32_t* page_indices, const int32_t* page_indptr,
+                                int32_t page_size, const int32_t* kv_indptr, void* out,
+                                float sm_scale, void* workspace, void* stream);
+int mla_decode_fp8_page_table(const void* q, const void* kv_fp8, const float* kv_scale,
+                              const int32_t* page_indices, const int32_t* page_indptr,
+                              int32_t page_size, const int32_t* kv_indptr, void* out,
+                              float sm_scale, void* workspace, void* stream);
+int mla_decode_bf16_page_table(const void* q, const void* kv_bf16, const int32_t* page_indices,
+                               const int32_t* page_indptr, int32_t page_size,
+                               const int32_t* kv_indptr, void* out, float sm_scale,
+                               void* workspace, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

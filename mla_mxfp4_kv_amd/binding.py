@@ -27,7 +27,8 @@ EXPORTS = (
     "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
     "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
     "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
-    "mla_decode_bf16_paged",
+    "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
+    "mla_decode_bf16_page_table",
 )
 
 _lib = None
@@ -73,10 +74,17 @@ def lib():
                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    # (q, pool, [scale,] page_indices, page_indptr, page_size, kv_indptr, out, sm_scale, workspace, stream)
+    pt = [ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_mxfp4_page_table.argtypes = pt
+    L.mla_decode_fp8_page_table.argtypes = pt
+    L.mla_decode_bf16_page_table.argtypes = pt[:1] + pt[2:]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
                  "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
                  "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
-                 "mla_decode_bf16_paged"):
+                 "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
+                 "mla_decode_bf16_page_table"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -207,6 +215,71 @@ def check_kv_indices(kv_indices, kv_indptr_host, pool_rows: int, row_bytes: int 
             raise ValueError("kv_indices holds rows outside the pool")
 
 
+def decode_page_table(fmt: str, q, pool, kv_scale, page_indices, page_indptr_dev, page_size: int, kv_indptr_dev,
+                      out, sm_scale: float, workspace, stream=None):
+    """Enqueue a decode over a page table (no checks; see ``MlaDecodePageTable``).
+    ``fmt``: "mxfp4" (pool = packed rows, kv_scale = E8M0 rows), "fp8" (kv_scale
+    = float32 [1]) or "bf16" (kv_scale unused)."""
+    head = [ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(pool.data_ptr())]
+    if fmt != "bf16":
+        head.append(ctypes.c_void_p(kv_scale.data_ptr()))
+    fn = f"mla_decode_{fmt}_page_table"
+    _check(getattr(lib(), fn)(
+        *head, ctypes.c_void_p(page_indices.data_ptr()), ctypes.c_void_p(page_indptr_dev.data_ptr()),
+        ctypes.c_int32(page_size), ctypes.c_void_p(kv_indptr_dev.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), fn)
+
+
+def page_table_kv_indptr(page_indptr, kv_last_page_len, page_size: int):
+    """Token offsets of a page table: sequence b holds (pages - 1) * page_size
+    + kv_last_page_len[b] tokens (none without pages). Checks that the page
+    offsets are non-decreasing from >= 0 and that every non-empty sequence's
+    last page holds 1..page_size rows."""
+    pi = [int(v) for v in page_indptr]
+    last = [int(v) for v in kv_last_page_len]
+    if page_size < 1:
+        raise ValueError("page_size must be >= 1")
+    if len(pi) < 1 or len(last) != len(pi) - 1:
+        raise ValueError("page_indptr needs batch + 1 entries and kv_last_page_len batch entries")
+    if pi[0] < 0 or any(b < a for a, b in zip(pi, pi[1:])):
+        raise ValueError("page_indptr must be non-decreasing from a value >= 0")
+    tok = [0]
+    for b in range(len(last)):
+        n = pi[b + 1] - pi[b]
+        if n > 0 and not 1 <= last[b] <= page_size:
+            raise ValueError(f"kv_last_page_len[{b}] = {last[b]} is not in [1, page_size]")
+        tok.append(tok[-1] + ((n - 1) * page_size + last[b] if n > 0 else 0))
+    if tok[-1] >= 2 ** 31:
+        raise ValueError("more than 2^31 - 1 tokens")
+    return tok
+
+
+def check_page_table(page_indices, page_indptr, kv_last_page_len, page_size: int, pool_rows: int,
+                     row_bytes: int = PACKED_BYTES):
+    """Host-side guard for page tables: int32 contiguous device page numbers
+    covering page_indptr[-1] entries, every row read inside the pool (a last
+    page needs only its valid rows), and a pool small enough for 32-bit
+    offsets (reads the pages back, one synchronisation)."""
+    import torch
+    if page_indices.dtype != torch.int32 or page_indices.dim() != 1 or not page_indices.is_contiguous():
+        raise ValueError("page_indices must be a contiguous int32 tensor")
+    pi = [int(v) for v in page_indptr]
+    last = [int(v) for v in kv_last_page_len]
+    if page_indices.numel() < pi[-1]:
+        raise ValueError("page_indices is shorter than page_indptr[-1]")
+    if pool_rows * row_bytes >= 2 ** 32:
+        raise ValueError("the row pool must be smaller than 2^32 bytes")
+    if pi[-1] > pi[0]:
+        pages = page_indices[pi[0]:pi[-1]].to(torch.int64)
+        # rows each page must hold: page_size, or the sequence's last-page count
+        need = torch.full_like(pages, page_size)
+        for b in range(len(last)):
+            if pi[b + 1] > pi[b]:
+                need[pi[b + 1] - 1 - pi[0]] = last[b]
+        if int(pages.min()) < 0 or int((pages * page_size + need).max()) > pool_rows:
+            raise ValueError("page_indices holds pages outside the pool")
+
+
 def decode_fp8(q, kv_fp8, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
     """Enqueue the fp8-cache decode (``kv_scale``: float32 [1] device tensor)."""
     _check(lib().mla_decode_fp8(
@@ -320,6 +393,65 @@ class MlaDecode:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode_bf16(q, kv_bf16, self.kv_indptr, out, sm_scale, self.workspace, stream)
         return out
+
+
+class MlaDecodePageTable:
+    """A planned decode over a page table: sequence b owns pages
+    ``page_indices[page_indptr[b]:page_indptr[b+1]]`` of ``page_size`` rows
+    each, the last holding ``kv_last_page_len[b]`` valid rows; token t is
+    pool row ``page * page_size + t % page_size`` of page ``t // page_size``.
+    ``page_indptr`` and ``kv_last_page_len`` are host lists/tensors (the plan
+    needs the token counts); the pools and ``page_indices`` are device
+    tensors passed per call."""
+
+    def __init__(self, page_indptr, kv_last_page_len, page_size: int, device="cuda", num_cus: int = 0):
+        import torch
+        tok = page_table_kv_indptr(page_indptr, kv_last_page_len, page_size)
+        self.page_size = int(page_size)
+        self.page_indptr_host = [int(v) for v in page_indptr]
+        self.last_host = [int(v) for v in kv_last_page_len]
+        self.plan = MlaDecode(tok, device=device, num_cus=num_cus)
+        self.batch = self.plan.batch
+        self.device = self.plan.device
+        self.kv_indptr = self.plan.kv_indptr
+        self.page_indptr = torch.tensor(self.page_indptr_host, dtype=torch.int32, device=self.device)
+
+    def _run(self, fmt, q, pool, kv_scale, page_indices, out, sm_scale, stream, check, row_bytes):
+        import torch
+        out = self.plan._out(q, out)
+        if fmt == "mxfp4":
+            _validate(q, pool, kv_scale, out, self.batch)
+        elif fmt == "fp8":
+            if pool.dtype not in (torch.uint8, torch.float8_e4m3fn) or pool.dim() != 2 \
+                    or pool.shape[1] != QK_DIM or not pool.is_contiguous():
+                raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [R,576]")
+            if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != pool.device:
+                raise ValueError("kv_scale must be a float32 device tensor of one element")
+        elif pool.dtype != torch.bfloat16 or pool.dim() != 2 or pool.shape[1] != QK_DIM \
+                or not pool.is_contiguous():
+            raise ValueError("kv_bf16 must be contiguous bfloat16 [R,576]")
+        if check:
+            check_page_table(page_indices, self.page_indptr_host, self.last_host, self.page_size,
+                             pool.shape[0], row_bytes)
+        decode_page_table(fmt, q, pool, kv_scale, page_indices, self.page_indptr, self.page_size,
+                          self.kv_indptr, out, sm_scale, self.plan.workspace, stream)
+        return out
+
+    def mxfp4(self, q, kv_packed, kv_scale, page_indices, out=None, sm_scale=1.0 / math.sqrt(576.0),
+              stream=None, check=True):
+        """MXFP4 decode: kv_packed uint8 [R,288], kv_scale uint8 [R,18] row pools."""
+        return self._run("mxfp4", q, kv_packed, kv_scale, page_indices, out, sm_scale, stream, check,
+                         PACKED_BYTES)
+
+    def fp8(self, q, kv_fp8, kv_scale, page_indices, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None,
+            check=True):
+        """fp8 decode: kv_fp8 uint8 E4M3 [R,576], kv_scale float32 [1]."""
+        return self._run("fp8", q, kv_fp8, kv_scale, page_indices, out, sm_scale, stream, check, QK_DIM)
+
+    def bf16(self, q, kv_bf16, page_indices, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None,
+             check=True):
+        """bf16 decode: kv_bf16 bfloat16 [R,576]."""
+        return self._run("bf16", q, kv_bf16, None, page_indices, out, sm_scale, stream, check, 2 * QK_DIM)
 
 
 class MlaDecodeDevicePlan:

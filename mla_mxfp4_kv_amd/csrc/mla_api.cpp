@@ -214,7 +214,8 @@ enum class KvFormat { kMxfp4, kFp8, kBf16 };
 // partial layout and the reduce kernel are the same for all of them.
 int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_scale,
                   const int32_t* kv_indices, const int32_t* kv_indptr, void* out, float sm_scale,
-                  void* workspace, void* stream, bool gather = false) {
+                  void* workspace, void* stream, bool gather = false,
+                  const int32_t* page_indptr = nullptr, int32_t page_size = 1) {
   int dev;
   DeviceInfo info;
   int st = current_device(&dev, &info);
@@ -246,6 +247,7 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
         return fail(MLA_ERR_INVALID, "kv_indices must be a non-null 4-byte aligned device pointer");
       if (fmt == KvFormat::kMxfp4 && !aligned(kv_scale, 2))
         return fail(MLA_ERR_INVALID, "kv_scale must be 2-byte aligned for a gathered cache");
+      if (page_size < 1) return fail(MLA_ERR_INVALID, "page_size must be >= 1");
     }
     if (fmt == KvFormat::kFp8 && (kv_scale == nullptr || !aligned(kv_scale, 4)))
       return fail(MLA_ERR_INVALID, "kv_scale must be a non-null 4-byte aligned device pointer");
@@ -256,6 +258,8 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   a.kv_scale = (const uint8_t*)kv_scale;
   a.kv_indptr = kv_indptr;
   a.kv_indices = gather ? kv_indices : nullptr;
+  a.page_indptr = gather ? page_indptr : nullptr;
+  a.page_size = gather ? page_size : 1;
   a.out = out;
   a.plan = (const int32_t*)workspace;
   a.part_lse = (float*)((uint8_t*)workspace + pe.off_lse);
@@ -277,6 +281,16 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   e = (hipError_t)mla::launch_reduce(a, stream);
   if (e != hipSuccess) return hip_fail(e, "mla_reduce_kernel launch");
   return MLA_OK;
+}
+
+// A page-table call needs its page offsets (checked before the plan, so an
+// empty batch reports the missing array too).
+bool page_table_ok(const int32_t* page_indptr) {
+  if (page_indptr == nullptr || !aligned(page_indptr, 4)) {
+    fail(MLA_ERR_INVALID, "page_indptr must be a non-null 4-byte aligned device pointer");
+    return false;
+  }
+  return true;
 }
 
 }  // namespace
@@ -317,6 +331,32 @@ int mla_decode_bf16_paged(const void* q, const void* kv_bf16, const int32_t* kv_
                           const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
   return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, kv_indices, kv_indptr, out, sm_scale, workspace,
                        stream, true);
+}
+
+int mla_decode_mxfp4_page_table(const void* q, const void* kv_packed, const void* kv_scale,
+                                const int32_t* page_indices, const int32_t* page_indptr, int32_t page_size,
+                                const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
+                                void* stream) {
+  if (!page_table_ok(page_indptr)) return MLA_ERR_INVALID;
+  return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, page_indices, kv_indptr, out, sm_scale,
+                       workspace, stream, true, page_indptr, page_size);
+}
+
+int mla_decode_fp8_page_table(const void* q, const void* kv_fp8, const float* kv_scale,
+                              const int32_t* page_indices, const int32_t* page_indptr, int32_t page_size,
+                              const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
+                              void* stream) {
+  if (!page_table_ok(page_indptr)) return MLA_ERR_INVALID;
+  return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, page_indices, kv_indptr, out, sm_scale, workspace,
+                       stream, true, page_indptr, page_size);
+}
+
+int mla_decode_bf16_page_table(const void* q, const void* kv_bf16, const int32_t* page_indices,
+                               const int32_t* page_indptr, int32_t page_size, const int32_t* kv_indptr,
+                               void* out, float sm_scale, void* workspace, void* stream) {
+  if (!page_table_ok(page_indptr)) return MLA_ERR_INVALID;
+  return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, page_indices, kv_indptr, out, sm_scale, workspace,
+                       stream, true, page_indptr, page_size);
 }
 
 }  // extern "C"

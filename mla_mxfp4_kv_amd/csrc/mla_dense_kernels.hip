@@ -188,7 +188,7 @@ __device__ __forceinline__ void lds_tr_x8(uint32_t addr, i32x2_t (&v)[8]) {
   }
 }
 
-// ---- per-token row lists (kv_indices, page size 1) ----------------------
+// ---- row lists and page tables (kv_indices) ------------------------------
 // A wave keeps the row indices of four tiles in a ring of 128-byte slots
 // after the tile buffers: the indices of tile i + 3 are loaded while tile
 // i is computed, so those of tile i + 1 have landed when its rows are
@@ -198,35 +198,45 @@ constexpr int kIdxWave = 4 * kIdxSlot;
 constexpr int kLdsGather = kLdsTotal + kWaves * kIdxWave;
 static_assert(kLdsGather <= 160 * 1024, "LDS budget of one gfx950 CU");
 
-// kv_indices[t0 .. t0 + kTile - 1] (the last valid one repeated past the
-// item's end) into `slot`, one 4-byte direct load per lane.
+// Row indices of a tile into `slot`, one 4-byte direct load per lane. The
+// tile starts `rel0` tokens into its sequence, whose entries in `indices`
+// start at `ibase`; tile row r (the last valid one repeated past the item's
+// end) takes entry ibase + (rel0 + r) / ps, its page. A per-token row list
+// is ps = 1 with ibase = the sequence's first token.
 template <bool kFp8>
-__device__ __forceinline__ void stage_idx(uint8_t* slot, const int32_t* __restrict__ kv_indices, int t0,
-                                          int nvalid, int lane) {
-  t0 = __builtin_amdgcn_readfirstlane(t0);
+__device__ __forceinline__ void stage_idx(uint8_t* slot, const int32_t* __restrict__ indices, int ibase,
+                                          int rel0, int nvalid, int ps, int lane) {
+  ibase = __builtin_amdgcn_readfirstlane(ibase);
+  rel0 = __builtin_amdgcn_readfirstlane(rel0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   if (lane < Cfg<kFp8>::kTile) {
     const int r = min(lane, nvalid - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(kv_indices + t0 + r), (MLA_LDS void*)slot, 4, 0, 0);
+    const int e = ps == 1 ? ibase + rel0 + r : ibase + (int)((uint32_t)(rel0 + r) / (uint32_t)ps);
+    __builtin_amdgcn_global_load_lds((const void*)(indices + e), (MLA_LDS void*)slot, 4, 0, 0);
   }
 }
 
 // Stage the tile whose row indices sit in `slot`: lane chunk c = 64*i + lane
 // of instruction i is 16-byte chunk c % (row/16) of tile row c / (row/16)
 // (rows past the item's end repeat the last valid row's last chunk). Lane r
-// reads index r once; the DMA lanes take theirs by cross-lane permute, so
-// the only LDS read is waited for inside its own block.
+// reads index r once (with pages, ps > 1, a page number that it turns into
+// the pool row page * ps + the row's offset in its page); the DMA lanes take
+// theirs by cross-lane permute, so the only LDS read is waited for inside
+// its own block.
 template <bool kFp8>
 __device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __restrict__ kv, const uint8_t* slot,
-                                             int nvalid, int lane) {
+                                             int rel0, int nvalid, int ps, int lane) {
   using C = Cfg<kFp8>;
   constexpr int kCpr = C::kRow / 16;
+  rel0 = __builtin_amdgcn_readfirstlane(rel0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   const int last = min(nvalid, C::kTile) - 1;
+  const int rl = min(lane, C::kTile - 1);
   uint32_t my;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
                : "=&v"(my)
-               : "v"(lds_addr(slot) + 4u * (uint32_t)min(lane, C::kTile - 1)));
+               : "v"(lds_addr(slot) + 4u * (uint32_t)rl));
+  if (ps != 1) my = my * (uint32_t)ps + (uint32_t)(rel0 + min(rl, last)) % (uint32_t)ps;
   uint32_t off[kDma];
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
@@ -477,9 +487,9 @@ template <bool kFp8, bool kGather>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                         const float* __restrict__ kv_scale, const int32_t* __restrict__ kv_indptr,
-                        const int32_t* __restrict__ kv_indices, uint16_t* __restrict__ out,
-                        const int32_t* __restrict__ plan, float* __restrict__ part_lse,
-                        float* __restrict__ part_out, float csc) {
+                        const int32_t* __restrict__ kv_indices, const int32_t* __restrict__ page_indptr,
+                        int page_size, uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
+                        float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
   using C = Cfg<kFp8>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kGather ? kLdsGather : kLdsTotal];
   const int tid = threadIdx.x;
@@ -509,6 +519,9 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
       const int kb = max(items[4 * it + 1], kv_indptr[b]);
       const int ke = min(items[4 * it + 2], kv_indptr[b + 1]);
       const int dest = items[4 * it + 3];
+      // first entry of the sequence in kv_indices: its page list, or its rows
+      const int seq_lo = kv_indptr[b];
+      const int ibase = kGather && page_indptr != nullptr ? page_indptr[b] : seq_lo;
       const int t_first = kb + C::kTile * wave;
       const int ntiles = t_first < ke ? (ke - t_first + C::kStride - 1) / C::kStride : 0;
 
@@ -596,20 +609,22 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
         uint8_t* islot = lds + kLdsTotal + wave * kIdxWave;
         auto tile_t0 = [&](int k) { return t_first + min(k, ntiles - 1) * C::kStride; };
         if (ntiles > 0) {
-          stage_idx<kFp8>(islot, kv_indices, tile_t0(0), ke - tile_t0(0), lane);
-          stage_idx<kFp8>(islot + kIdxSlot, kv_indices, tile_t0(1), ke - tile_t0(1), lane);
+          stage_idx<kFp8>(islot, kv_indices, ibase, tile_t0(0) - seq_lo, ke - tile_t0(0), page_size, lane);
+          stage_idx<kFp8>(islot + kIdxSlot, kv_indices, ibase, tile_t0(1) - seq_lo, ke - tile_t0(1), page_size,
+                          lane);
           wait_vm<0>();
-          stage_gather<kFp8>(ring, kv, islot, ke - t_first, lane);
-          stage_idx<kFp8>(islot + 2 * kIdxSlot, kv_indices, tile_t0(2), ke - tile_t0(2), lane);
+          stage_gather<kFp8>(ring, kv, islot, t_first - seq_lo, ke - t_first, page_size, lane);
+          stage_idx<kFp8>(islot + 2 * kIdxSlot, kv_indices, ibase, tile_t0(2) - seq_lo, ke - tile_t0(2),
+                          page_size, lane);
         }
         for (int i = 0; i < ntiles; ++i) {
           if (i + 1 < ntiles) {
             wait_vm<kDma + 1>();   // indices of tile i + 1 (then: rows of i, indices of i + 2)
             const int tn = t_first + (i + 1) * C::kStride;
-            stage_gather<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv, islot + ((i + 1) & 3) * kIdxSlot, ke - tn,
-                               lane);
-            stage_idx<kFp8>(islot + ((i + 3) & 3) * kIdxSlot, kv_indices, tile_t0(i + 3), ke - tile_t0(i + 3),
-                            lane);
+            stage_gather<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv, islot + ((i + 1) & 3) * kIdxSlot,
+                               tn - seq_lo, ke - tn, page_size, lane);
+            stage_idx<kFp8>(islot + ((i + 3) & 3) * kIdxSlot, kv_indices, ibase, tile_t0(i + 3) - seq_lo,
+                            ke - tile_t0(i + 3), page_size, lane);
             wait_vm<kDma + 2>();   // rows of tile i (then: indices of i + 2, rows of i + 1, indices of i + 3)
           } else {
             wait_vm<0>();
@@ -703,6 +718,7 @@ template <bool kFp8, bool kGather>
 static void launch_dense(const DecodeArgs& a, const float* kv_scale, void* stream) {
   hipLaunchKernelGGL((mla_decode_dense_kernel<kFp8, kGather>), dim3(a.grid), dim3(kThreads), 0,
                      (hipStream_t)stream, (const uint16_t*)a.q, a.kv_packed, kv_scale, a.kv_indptr, a.kv_indices,
+                     kGather ? a.page_indptr : (const int32_t*)nullptr, kGather ? a.page_size : 1,
                      (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
 }
 

@@ -66,7 +66,10 @@ struct DecodeArgs {
   const uint8_t* kv_packed;
   const uint8_t* kv_scale;
   const int32_t* kv_indptr;
-  const int32_t* kv_indices;   // per-token cache rows (nullptr: contiguous sequences)
+  const int32_t* kv_indices;   // per-token cache rows, or pages (nullptr: contiguous sequences)
+  const int32_t* page_indptr;  // with pages: sequence b's pages start at kv_indices[page_indptr[b]]
+                               // (nullptr: kv_indices lists one row per token)
+  int32_t page_size;           // rows per page (1 for a per-token row list)
   void* out;
   const int32_t* plan;    // device plan words (workspace start)
   float* part_lse;

@@ -176,17 +176,22 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
   stage_dma<0, kRowDma, true>(buf, kv, sc, t0, nvalid, lane);
 }
 
-// Row indices of the tile starting at token t0 (kv_indices[t0 .. t0 + 31],
-// the last valid one repeated past the item's end) into the buffer's index
-// slot: one 4-byte direct load per lane of the first 32.
-__device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restrict__ kv_indices, int t0,
-                                          int nvalid, int lane) {
-  t0 = __builtin_amdgcn_readfirstlane(t0);
+// Row indices of a tile into the buffer's index slot, one 4-byte direct
+// load per lane of the first 32. The tile starts `rel0` tokens into its
+// sequence, whose entries in `indices` start at `ibase`; tile row r (the
+// last valid one repeated past the item's end) takes entry
+// ibase + (rel0 + r) / ps, its page. A per-token row list is ps = 1 with
+// ibase = the sequence's first token, so the entry is the token's own row.
+__device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restrict__ indices, int ibase,
+                                          int rel0, int nvalid, int ps, int lane) {
+  ibase = __builtin_amdgcn_readfirstlane(ibase);
+  rel0 = __builtin_amdgcn_readfirstlane(rel0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   if (lane < kTile) {
     const int r = min(lane, nvalid - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(kv_indices + t0 + r),
-                                     (MLA_LDS void*)(buf + Lds<true>::kIdx), 4, 0, 0);
+    const int e = ps == 1 ? ibase + rel0 + r : ibase + (int)((uint32_t)(rel0 + r) / (uint32_t)ps);
+    __builtin_amdgcn_global_load_lds((const void*)(indices + e), (MLA_LDS void*)(buf + Lds<true>::kIdx), 4, 0,
+                                     0);
   }
 }
 
@@ -196,11 +201,20 @@ __device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restric
 // row's 18 scale bytes come as the two aligned 16-byte chunks that cover
 // them (an 18-byte row starts at an even offset, so two always suffice)
 // into the row's 32-byte slot. All indices are read before any load is
-// issued.
+// issued. With pages (ps > 1) the slot first has its page numbers turned
+// into pool rows, page * ps + the row's offset in its page, for every later
+// reader of the slot.
 __device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __restrict__ kv,
-                                             const uint8_t* __restrict__ sc, int nvalid, int lane) {
+                                             const uint8_t* __restrict__ sc, int rel0, int nvalid, int ps,
+                                             int lane) {
+  rel0 = __builtin_amdgcn_readfirstlane(rel0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   const int last = min(nvalid, kTile) - 1;
+  if (ps != 1 && lane < kTile) {
+    int32_t* slot = (int32_t*)(buf + Lds<true>::kIdx);
+    const uint32_t in_page = (uint32_t)(rel0 + min(lane, last)) % (uint32_t)ps;
+    slot[lane] = (int32_t)((uint32_t)slot[lane] * (uint32_t)ps + in_page);
+  }
   const int32_t* idx = (const int32_t*)(buf + Lds<true>::kIdx);
   uint32_t off[kRowDma];
 #pragma unroll
@@ -619,9 +633,9 @@ template <bool kGather>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
-                  const int32_t* __restrict__ kv_indices, uint16_t* __restrict__ out,
-                  const int32_t* __restrict__ plan, float* __restrict__ part_lse,
-                  float* __restrict__ part_out, float csc) {
+                  const int32_t* __restrict__ kv_indices, const int32_t* __restrict__ page_indptr,
+                  int page_size, uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
+                  float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
   using L = Lds<kGather>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::kTotal];
   const int tid = threadIdx.x;
@@ -652,6 +666,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int kb = max(items[4 * it + 1], seq_lo);
       const int ke = min(items[4 * it + 2], seq_hi);
       const int dest = items[4 * it + 3];
+      // first entry of the sequence in kv_indices: its page list, or its rows
+      const int ibase = kGather && page_indptr != nullptr ? page_indptr[b] : seq_lo;
 
       const int len = ke - kb;
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
@@ -677,11 +693,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         if (ntiles > 0) {
           if constexpr (kGather) {
             // row indices of the first two tiles, then tile 0 from them
-            stage_idx(ring, kv_indices, t_first, ke - t_first, lane);
+            stage_idx(ring, kv_indices, ibase, t_first - seq_lo, ke - t_first, page_size, lane);
             if (ntiles > 1)
-              stage_idx(ring + L::kBuf, kv_indices, t_first + kTileStride, ke - t_first - kTileStride, lane);
+              stage_idx(ring + L::kBuf, kv_indices, ibase, t_first + kTileStride - seq_lo,
+                        ke - t_first - kTileStride, page_size, lane);
             wait_dma();
-            stage_gather(ring, kv, sc, ke - t_first, lane);
+            stage_gather(ring, kv, sc, t_first - seq_lo, ke - t_first, page_size, lane);
           } else {
             stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
           }
@@ -696,10 +713,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
               // tile i + 1 from the indices staged a round ago; the indices
               // of tile i + 2 go to the slot of the buffer it will use (the
               // P V wave reads only that buffer's rows this round)
-              stage_gather(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, ke - tn, lane);
+              stage_gather(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn - seq_lo, ke - tn, page_size, lane);
               if (i + 2 < ntiles)
-                stage_idx(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, tn + kTileStride,
-                          ke - tn - kTileStride, lane);
+                stage_idx(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, ibase, tn + kTileStride - seq_lo,
+                          ke - tn - kTileStride, page_size, lane);
             } else {
               stage_dma(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn, ke - tn, lane);
             }
@@ -948,11 +965,13 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   if (a.kv_indices != nullptr) {
     hipLaunchKernelGGL(mla_decode_kernel<true>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, a.kv_indices,
-                       (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+                       a.page_indptr, a.page_size, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
+                       a.score_scale_log2);
   } else {
     hipLaunchKernelGGL(mla_decode_kernel<false>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (const int32_t*)nullptr,
-                       (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+                       (const int32_t*)nullptr, 1, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
+                       a.score_scale_log2);
   }
   return (int)hipGetLastError();
 }

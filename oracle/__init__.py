@@ -24,6 +24,8 @@ Modules:
   also over per-token row lists (``mla_decode_ref_gather``).
 * :mod:`oracle.dense_ref` -- exact fp8 (e4m3 + per-tensor scale) and bf16
   cache decoding and the same fp64 attention, for the sibling decodes.
+* :mod:`oracle.paging_ref` -- page tables (page number, page size, valid rows
+  of the last page) expanded to pool rows, page by page.
 * :mod:`oracle.planner_ref` -- the CPU reference work-list planner.
 
 Page "kernelbot-amd-mixed-mla-676098" also gives the fp8 cache (``_aiter_mla_decode``:
@@ -45,6 +47,7 @@ from .mxfp4_ref import (  # noqa: F401
     mla_decode_ref,
     mla_decode_ref_seq,
     mla_decode_ref_gather,
+    mla_decode_ref_page_table,
 )
 from .dense_ref import (  # noqa: F401
     E4M3_VALUES,
@@ -57,5 +60,8 @@ from .dense_ref import (  # noqa: F401
     mla_decode_ref_fp8_seq,
     mla_decode_ref_bf16,
     mla_decode_ref_bf16_seq,
+    mla_decode_ref_fp8_page_table,
+    mla_decode_ref_bf16_page_table,
 )
+from .paging_ref import page_table_rows, page_table_token_indptr  # noqa: F401
 from .planner_ref import plan_words_ref, PlanRef, decode_plan_words  # noqa: F401

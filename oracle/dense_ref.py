@@ -126,3 +126,26 @@ def mla_decode_ref_bf16(q, bits, kv_indptr, sm_scale: float, batches=None):
     """Oracle for a batch over a bf16 cache: float64 [B, 16, 512]."""
     return _batched(lambda qb, lo, hi: mla_decode_ref_bf16_seq(qb, bits[lo:hi], sm_scale),
                     q, kv_indptr, batches)
+
+
+def _page_table(fn, q, page_indices, page_indptr, kv_last_page_len, page_size, batches):
+    from .paging_ref import page_table_rows
+    rows = page_table_rows(page_indices, page_indptr, kv_last_page_len, page_size)
+    out = np.full((len(rows), NUM_HEADS, V_DIM), np.nan, dtype=np.float64)
+    for b in (range(len(rows)) if batches is None else batches):
+        out[b] = fn(np.asarray(q)[b], rows[b])
+    return out
+
+
+def mla_decode_ref_fp8_page_table(q, codes, kv_scale, page_indices, page_indptr, kv_last_page_len,
+                                  page_size: int, sm_scale: float, batches=None):
+    """fp8 oracle over a page table (``oracle.paging_ref``): float64 [B, 16, 512]."""
+    return _page_table(lambda qb, r: mla_decode_ref_fp8_seq(qb, np.asarray(codes)[r], kv_scale, sm_scale),
+                       q, page_indices, page_indptr, kv_last_page_len, page_size, batches)
+
+
+def mla_decode_ref_bf16_page_table(q, bits, page_indices, page_indptr, kv_last_page_len, page_size: int,
+                                   sm_scale: float, batches=None):
+    """bf16 oracle over a page table: float64 [B, 16, 512]."""
+    return _page_table(lambda qb, r: mla_decode_ref_bf16_seq(qb, np.asarray(bits)[r], sm_scale),
+                       q, page_indices, page_indptr, kv_last_page_len, page_size, batches)

@@ -159,3 +159,16 @@ def mla_decode_ref_gather(q, packed, scales, kv_indices, kv_indptr, sm_scale: fl
         rows = idx[int(indptr[b]):int(indptr[b + 1])]
         out[b] = mla_decode_ref_seq(q[b], np.asarray(packed)[rows], np.asarray(scales)[rows], sm_scale)
     return out
+
+
+def mla_decode_ref_page_table(q, packed, scales, page_indices, page_indptr, kv_last_page_len,
+                              page_size: int, sm_scale: float, batches=None) -> np.ndarray:
+    """Oracle over a page table (``oracle.paging_ref``): each sequence's pool
+    rows, page by page, then the same definition. float64 [B, 16, 512]."""
+    from .paging_ref import page_table_rows
+    rows = page_table_rows(page_indices, page_indptr, kv_last_page_len, page_size)
+    q = np.asarray(q)
+    out = np.full((len(rows), NUM_HEADS, V_DIM), np.nan, dtype=np.float64)
+    for b in (range(len(rows)) if batches is None else batches):
+        out[b] = mla_decode_ref_seq(q[b], np.asarray(packed)[rows[b]], np.asarray(scales)[rows[b]], sm_scale)
+    return out

@@ -1,0 +1,256 @@
+"""GPU parity of the decodes over page tables (mla_decode_mxfp4_page_table,
+mla_decode_fp8_page_table, mla_decode_bf16_page_table) against the fp64
+page-table oracle, through the C ABI, and bit-identity with the row-list
+decodes reading the same rows. Same bar as the contiguous decodes."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mla_mxfp4_kv_amd import binding, synth
+from oracle import dense_ref as dref
+from oracle import mxfp4_ref as ref
+from oracle import paging_ref as pref
+
+pytestmark = pytest.mark.gpu
+
+SM = 1.0 / math.sqrt(576.0)
+ATOL = 1e-2
+RTOL = 1e-2
+NORMWISE = 5e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+    yield
+
+
+def _qbits(q):
+    return q.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check(got, want, label):
+    nan_w = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan_w), f"{label}: NaN pattern differs"
+    g, w = got[~nan_w], want[~nan_w]
+    err = np.abs(g - w)
+    assert np.all(err <= ATOL + RTOL * np.abs(w)), f"{label}: max err {float(err.max()):.3e}"
+    den = np.linalg.norm(w)
+    if den > 0:
+        nw = np.linalg.norm(g - w) / den
+        assert nw <= NORMWISE, f"{label}: normwise {nw:.3e}"
+
+
+def _table(lens, ps, seed, extra=2):
+    """A page table for sequences of `lens` tokens: page offsets, valid rows
+    of each last page, and the pool slot of every page (random, over
+    `extra` times as many slots as pages)."""
+    npages = [(n + ps - 1) // ps for n in lens]
+    pi = np.concatenate([[0], np.cumsum(npages)]).astype(np.int64)
+    last = [n - (p - 1) * ps if p else 0 for n, p in zip(lens, npages)]
+    slots = max(1, extra * int(pi[-1]))
+    pages = np.random.default_rng(seed).permutation(slots)[: int(pi[-1])].astype(np.int32)
+    return pi, last, pages, slots
+
+
+def _fill(pool, cache, indptr, pi, pages, ps, lens):
+    """Copy each sequence's contiguous rows into its pages of the pool."""
+    for b, n in enumerate(lens):
+        lo = int(indptr[b])
+        for j in range((n + ps - 1) // ps):
+            used = min(ps, n - j * ps)
+            r0 = int(pages[int(pi[b]) + j]) * ps
+            pool[r0:r0 + used] = cache[lo + j * ps:lo + j * ps + used]
+
+
+def _case(fmt, lens, ps, seed):
+    pi, last, pages, slots = _table(lens, ps, seed)
+    rows = slots * ps
+    rng = np.random.default_rng(seed + 1)
+    w = synth.Workload("p", len(lens), None, None, 1.0, False, seed)
+    if fmt == "mxfp4":
+        q, packed, scales, indptr, _ = synth.make_inputs(w, lengths=lens)
+        pool = (torch.from_numpy(rng.integers(0, 256, (rows, 288), dtype=np.uint8)),
+                torch.from_numpy(rng.integers(118, 136, (rows, 18), dtype=np.uint8)))
+        _fill(pool[0], packed, indptr, pi, pages, ps, lens)
+        _fill(pool[1], scales, indptr, pi, pages, ps, lens)
+        scale = None
+    else:
+        q, cache, scale, indptr, _ = synth.make_dense_inputs(w, fmt, lengths=lens)
+        if fmt == "fp8":
+            p = torch.from_numpy(rng.integers(0, 0x7E, (rows, 576), dtype=np.uint8))
+        else:
+            p = torch.randn(rows, 576, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+        _fill(p, cache, indptr, pi, pages, ps, lens)
+        pool = (p,)
+    return q, pool, scale, indptr, pi, last, pages
+
+
+def _oracle(fmt, q, pool, scale, pi, last, pages, ps, batches=None):
+    qb = _qbits(q)
+    if fmt == "mxfp4":
+        return ref.mla_decode_ref_page_table(qb, pool[0].numpy(), pool[1].numpy(), pages, pi, last, ps, SM,
+                                             batches=batches)
+    if fmt == "fp8":
+        return dref.mla_decode_ref_fp8_page_table(qb, pool[0].numpy(), float(scale[0]), pages, pi, last, ps,
+                                                  SM, batches=batches)
+    bits = pool[0].view(torch.int16).numpy().view(np.uint16)
+    return dref.mla_decode_ref_bf16_page_table(qb, bits, pages, pi, last, ps, SM, batches=batches)
+
+
+def _run(dec, fmt, q, pool, scale, pages, **kw):
+    if fmt == "mxfp4":
+        return dec.mxfp4(q, pool[0], pool[1], pages, sm_scale=SM, **kw)
+    if fmt == "fp8":
+        return dec.fp8(q, pool[0], scale, pages, sm_scale=SM, **kw)
+    return dec.bf16(q, pool[0], pages, sm_scale=SM, **kw)
+
+
+def _run_rows(fmt, indptr, q, pool, scale, rows, num_cus):
+    dec = binding.MlaDecode(indptr, device="cuda", num_cus=num_cus)
+    if fmt == "mxfp4":
+        return dec.mxfp4_paged(q, pool[0], pool[1], rows, sm_scale=SM)
+    if fmt == "fp8":
+        return dec.fp8_paged(q, pool[0], scale, rows, sm_scale=SM)
+    return dec.bf16_paged(q, pool[0], rows, sm_scale=SM)
+
+
+# (lengths, page size, CUs the plan is spread over; 0 = the device's)
+CASES = [
+    ([1], 16, 0),
+    ([31, 32, 33], 16, 0),
+    ([127, 128, 129], 7, 3),
+    ([0, 300, 0, 1000], 64, 0),
+    ([5000], 16, 0),
+    ([1, 1, 1, 1, 700], 1, 7),
+    ([257, 4097, 33, 2000], 32, 0),
+    ([100, 200], 100, 2),
+]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8", "bf16"])
+@pytest.mark.parametrize("lens,ps,num_cus", CASES)
+def test_page_table_matches_oracle(fmt, lens, ps, num_cus):
+    """Element-wise against the page-table oracle, and bit for bit against
+    the row-list decode of the same rows (the same kernels read the same
+    bytes in the same order)."""
+    _say(f"case page table {fmt} lens={lens} page_size={ps} num_cus={num_cus}")
+    q, pool, scale, indptr, pi, last, pages = _case(fmt, lens, ps, seed=sum(lens) + ps)
+    dec = binding.MlaDecodePageTable(pi.tolist(), last, ps, device="cuda", num_cus=num_cus)
+    assert dec.kv_indptr.cpu().tolist() == indptr.tolist()
+    qd = q.cuda()
+    dpool = tuple(p.cuda() for p in pool)
+    dscale = scale.cuda() if scale is not None else None
+    out = _run(dec, fmt, qd, dpool, dscale, torch.from_numpy(pages).cuda())
+    torch.cuda.synchronize()
+    _check(out.float().cpu().numpy(), _oracle(fmt, q, pool, scale, pi, last, pages, ps), f"{fmt} {lens} ps={ps}")
+    rows = np.concatenate(pref.page_table_rows(pages, pi, last, ps) + [np.zeros(0, np.int64)])
+    rows = torch.from_numpy(rows.astype(np.int32)).cuda()
+    same = _run_rows(fmt, indptr.tolist(), qd, dpool, dscale, rows, num_cus)
+    torch.cuda.synchronize()
+    assert torch.equal(out, same), f"{fmt} {lens} ps={ps}: page table and row list differ"
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_headline_workload_in_16_row_pages(fmt):
+    """B=256, kv=8192 with every sequence in shuffled 16-row pages: bit
+    identical to the row-list decode of the same rows, and to the oracle on
+    sampled sequences."""
+    w = synth.WORKLOADS["b256_kv8192"]
+    ps = 16
+    _say(f"case page table b256_kv8192 {fmt}: generating")
+    if fmt == "mxfp4":
+        q, packed, scales, indptr, lens = synth.make_inputs(w, device="cuda")
+        cache = (packed, scales)
+        scale = None
+    else:
+        q, c, scale, indptr, lens = synth.make_dense_inputs(w, fmt, device="cuda")
+        cache = (c,)
+    t = int(indptr[-1])
+    npages = t // ps
+    assert t % ps == 0 and all(int(n) % ps == 0 for n in lens)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    pages = torch.randperm(npages, generator=g).to(torch.int32).cuda()
+    rows = (pages.long().repeat_interleave(ps) * ps + torch.arange(ps, device="cuda").repeat(npages))
+    pool = tuple(torch.empty_like(x) for x in cache)
+    for p, x in zip(pool, cache):
+        p[rows] = x
+    pi = [int(v) // ps for v in indptr]
+    last = [ps if int(n) else 0 for n in lens]
+    dec = binding.MlaDecodePageTable(pi, last, ps, device="cuda")
+    _say(f"case page table b256_kv8192 {fmt}: decode")
+    out = _run(dec, fmt, q, pool, scale, pages)
+    same = _run_rows(fmt, indptr.tolist(), q, pool, scale, rows.to(torch.int32), 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, same)
+    got = out.float().cpu().numpy()
+    qb = _qbits(q)
+    for b in (0, 200):
+        lo, hi = int(indptr[b]), int(indptr[b + 1])
+        if fmt == "mxfp4":
+            want = ref.mla_decode_ref_seq(qb[b], cache[0][lo:hi].cpu().numpy(), cache[1][lo:hi].cpu().numpy(),
+                                          w.sm_scale)
+        else:
+            want = dref.mla_decode_ref_fp8_seq(qb[b], cache[0][lo:hi].cpu().numpy(), float(scale[0]), w.sm_scale)
+        _check(got[b], want, f"b256 page table {fmt} b={b}")
+
+
+def test_graph_replays_page_table_decode():
+    """The page-table decode captured in a HIP graph (host plan, checks done
+    before capture) replays to the eager result, with eager work between
+    the replays."""
+    _say("case page table graph replay")
+    lens, ps = [300, 0, 1500, 77], 16
+    q, pool, scale, indptr, pi, last, pages = _case("mxfp4", lens, ps, seed=41)
+    dec = binding.MlaDecodePageTable(pi.tolist(), last, ps, device="cuda", num_cus=5)
+    qd, dpool, dpages = q.cuda(), tuple(p.cuda() for p in pool), torch.from_numpy(pages).cuda()
+    out = torch.empty(len(lens), 16, 512, dtype=torch.bfloat16, device="cuda")
+    eager = _run(dec, "mxfp4", qd, dpool, None, dpages, out=out).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        _run(dec, "mxfp4", qd, dpool, None, dpages, out=out, stream=s, check=False)   # warm the stream
+        s.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            _run(dec, "mxfp4", qd, dpool, None, dpages, out=out, stream=s, check=False)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {k}"
+
+
+def test_page_table_errors():
+    _say("case page table errors")
+    lens, ps = [40], 16
+    q, pool, scale, indptr, pi, last, pages = _case("mxfp4", lens, ps, seed=3)
+    dec = binding.MlaDecodePageTable(pi.tolist(), last, ps, device="cuda")
+    qd, dpool, dpages = q.cuda(), tuple(p.cuda() for p in pool), torch.from_numpy(pages).cuda()
+    with pytest.raises(ValueError):   # a page past the pool
+        _run(dec, "mxfp4", qd, dpool, None, dpages + 1000)
+    with pytest.raises(ValueError):   # fewer pages than the offsets say
+        _run(dec, "mxfp4", qd, dpool, None, dpages[:1])
+    out = torch.empty(1, 16, 512, dtype=torch.bfloat16, device="cuda")
+    ptr = lambda t: binding.ctypes.c_void_p(t.data_ptr())
+    L = binding.lib()
+    args = (ptr(qd), ptr(dpool[0]), ptr(dpool[1]), ptr(dpages))
+    tail = (ptr(dec.kv_indptr), ptr(out), SM, ptr(dec.plan.workspace), None)
+    assert L.mla_decode_mxfp4_page_table(*args, ptr(dec.page_indptr), 0, *tail) == -1   # page size 0
+    assert L.mla_decode_mxfp4_page_table(*args, None, ps, *tail) == -1                  # no page offsets
+    assert L.mla_decode_mxfp4_page_table(*args[:3], None, ptr(dec.page_indptr), ps, *tail) == -1
+    assert L.mla_decode_mxfp4_page_table(*args, ptr(dec.page_indptr), ps, *tail) == 0
+    torch.cuda.synchronize()

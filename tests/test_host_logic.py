@@ -79,3 +79,33 @@ def test_dense_inputs_share_the_mxfp4_draws():
     assert lat.shape == (7, 576) and lat.dtype == torch.bfloat16
     with pytest.raises(ValueError):
         synth.make_dense_inputs(w, "fp4", lengths=[3, 4])
+
+
+def test_page_table_offsets_and_guards():
+    """Token offsets of a page table and the binding's checks of it (host
+    only: the checks read CPU tensors just like device ones)."""
+    import torch
+    from mla_mxfp4_kv_amd import binding
+    assert binding.page_table_kv_indptr([0, 3, 3, 4], [3, 0, 4], 4) == [0, 11, 11, 15]
+    assert binding.page_table_kv_indptr([2, 2], [0], 16) == [0, 0]
+    for pi, last, ps in (([0, 1], [0], 4),      # a page with no rows
+                         ([0, 1], [5], 4),      # more rows than the page holds
+                         ([0, 2, 1], [1, 1], 4),  # offsets going down
+                         ([0, 1], [1], 0)):     # page size 0
+        with pytest.raises(ValueError):
+            binding.page_table_kv_indptr(pi, last, ps)
+    pages = torch.tensor([7, 2, 5, 0], dtype=torch.int32)
+    # sequence 0's last page 5 needs rows 20..22, sequence 2's page 0 rows 0..3
+    binding.check_page_table(pages, [0, 3, 3, 4], [3, 0, 4], 4, pool_rows=32)
+    with pytest.raises(ValueError):   # page 7 (a full page) needs rows up to 31
+        binding.check_page_table(pages, [0, 3, 3, 4], [3, 0, 4], 4, pool_rows=31)
+    last_page_seven = torch.tensor([2, 7], dtype=torch.int32)
+    binding.check_page_table(last_page_seven, [0, 2], [2], 4, pool_rows=30)   # rows 28, 29
+    with pytest.raises(ValueError):
+        binding.check_page_table(last_page_seven, [0, 2], [3], 4, pool_rows=30)
+    with pytest.raises(ValueError):   # negative page
+        binding.check_page_table(torch.tensor([-1], dtype=torch.int32), [0, 1], [1], 4, pool_rows=64)
+    with pytest.raises(ValueError):   # table shorter than its offsets
+        binding.check_page_table(torch.tensor([0], dtype=torch.int32), [0, 2], [1], 4, pool_rows=64)
+    with pytest.raises(ValueError):   # wrong dtype
+        binding.check_page_table(torch.tensor([0], dtype=torch.int64), [0, 1], [1], 4, pool_rows=64)
