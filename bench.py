@@ -97,14 +97,16 @@ QO_BYTES_PER_SEQ = 16 * 576 * 2 + 16 * 512 * 2
 PARTIAL_BYTES = 16 * (512 + 1) * 4
 
 
-def algorithmic_bytes(words, total_tokens, fmt="mxfp4", gather=False):
+def algorithmic_bytes(words, total_tokens, fmt="mxfp4", gather=False, pages=None):
     """Bytes the decode must move: KV (+ scales), Q, output, each split
     partial written once and read once, and with a gathered cache the
-    4-byte row index of every token."""
+    4-byte row index of every token (or, through a page table, the 4-byte
+    entry of every page: ``pages`` entries)."""
     num_partials = words[9]
     batch = words[2]
+    index = 4 * pages if pages is not None else (4 * total_tokens if gather else 0)
     return (synth.kv_bytes(total_tokens, fmt) + batch * QO_BYTES_PER_SEQ
-            + 2 * num_partials * PARTIAL_BYTES + (4 * total_tokens if gather else 0))
+            + 2 * num_partials * PARTIAL_BYTES + index)
 
 
 def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=None):
@@ -167,6 +169,10 @@ def main(argv=None):
     ap.add_argument("--gather", type=int, default=0, metavar="PAGE",
                     help="scatter the rows over the pool in pages of PAGE rows (seeded shuffle) and "
                          "decode through per-token kv_indices (the *_paged entry points)")
+    ap.add_argument("--page-table", type=int, default=0, metavar="PAGE",
+                    help="store every sequence in pages of PAGE rows (the last one partial), pages "
+                         "shuffled over the pool (seeded), and decode through the page table (the "
+                         "*_page_table entry points)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
@@ -224,7 +230,41 @@ def main(argv=None):
         binding.check_kv_indices(kv_indices, indptr.tolist(), packed.shape[0],
                                  packed.shape[1] * packed.element_size())
         torch.cuda.synchronize()
-    if kv_indices is not None and fmt == "mxfp4":
+    page_table = None
+    if args.page_table:
+        if args.gather:
+            print("--gather and --page-table are exclusive", file=sys.stderr)
+            return 2
+        ps = args.page_table
+        lens_t = torch.tensor([int(n) for n in lens], dtype=torch.int64)
+        npages = (lens_t + ps - 1) // ps
+        pi = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(npages, 0)])
+        last = torch.where(npages > 0, lens_t - (npages - 1) * ps, torch.zeros_like(lens_t))
+        g = torch.Generator().manual_seed(1234)
+        pages = torch.randperm(int(pi[-1]), generator=g).to(torch.int32)
+        # token -> pool row: page of the token's run within its sequence
+        seq = torch.repeat_interleave(torch.arange(w.batch), lens_t)
+        rel = torch.arange(total) - torch.as_tensor(indptr.tolist()[:-1], dtype=torch.int64)[seq]
+        rows = pages[pi[seq] + rel // ps].to(torch.int64) * ps + rel % ps
+        rows = rows.to(dev)
+        pool_p = torch.empty((int(pi[-1]) * ps,) + tuple(packed.shape[1:]), dtype=packed.dtype, device=dev)
+        pool_p[rows] = packed
+        if fmt == "mxfp4":
+            pool_s = torch.empty((pool_p.shape[0], scales.shape[1]), dtype=scales.dtype, device=dev)
+            pool_s[rows] = scales
+            scales = pool_s
+        packed = pool_p
+        page_table = binding.MlaDecodePageTable(pi.tolist(), last.tolist(), ps, device=dev)
+        pages_dev = pages.to(dev)
+        binding.check_page_table(pages_dev, pi.tolist(), last.tolist(), ps, packed.shape[0],
+                                 packed.shape[1] * packed.element_size())
+        torch.cuda.synchronize()
+        dec = page_table.plan
+
+        def call():
+            binding.decode_page_table(fmt, q, packed, scales, pages_dev, page_table.page_indptr, ps,
+                                      dec.kv_indptr, out, w.sm_scale, dec.workspace)
+    elif kv_indices is not None and fmt == "mxfp4":
         def call():
             binding.decode_mxfp4_paged(q, packed, scales, kv_indices, dec.kv_indptr, out, w.sm_scale,
                                        dec.workspace)
@@ -296,7 +336,8 @@ def main(argv=None):
     # wall clock includes the flushes, so the event time is used instead
     step_s = (avg_us * 1e-6) if args.cold else (wall / args.steps)
     value = kvb / step_s / 1e9
-    alg = algorithmic_bytes(words, total, fmt, kv_indices is not None)
+    alg = algorithmic_bytes(words, total, fmt, kv_indices is not None,
+                            page_table.page_indptr_host[-1] if page_table is not None else None)
     achieved = alg / (avg_us * 1e-6) / 1e9
 
     cpu = None
@@ -330,6 +371,7 @@ def main(argv=None):
             "workload": w.name,
             "kv_format": fmt,
             "gather_page_rows": args.gather or None,
+            "page_table_rows": args.page_table or None,
             "batch": w.batch,
             "kv_len": w.kv_len if w.kv_len is not None else f"U{list(w.ragged)}",
             "total_tokens": total,
@@ -346,8 +388,8 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if args.gather else measured_traffic(w.name, fmt),
-            "kernel": GATHER_KERNEL_NAME[fmt] if args.gather else KERNEL_NAME[fmt],
+            "traffic": None if (args.gather or args.page_table) else measured_traffic(w.name, fmt),
+            "kernel": GATHER_KERNEL_NAME[fmt] if (args.gather or args.page_table) else KERNEL_NAME[fmt],
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_source_sha256": kernel_source_hash(fmt),

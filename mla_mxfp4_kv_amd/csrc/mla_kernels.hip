@@ -182,6 +182,9 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
 // last valid one repeated past the item's end) takes entry
 // ibase + (rel0 + r) / ps, its page. A per-token row list is ps = 1 with
 // ibase = the sequence's first token, so the entry is the token's own row.
+// kPages selects the page-table form at compile time (the row-list kernel
+// then carries none of the page arithmetic).
+template <bool kPages>
 __device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restrict__ indices, int ibase,
                                           int rel0, int nvalid, int ps, int lane) {
   ibase = __builtin_amdgcn_readfirstlane(ibase);
@@ -189,7 +192,7 @@ __device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restric
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   if (lane < kTile) {
     const int r = min(lane, nvalid - 1);
-    const int e = ps == 1 ? ibase + rel0 + r : ibase + (int)((uint32_t)(rel0 + r) / (uint32_t)ps);
+    const int e = kPages ? ibase + (int)((uint32_t)(rel0 + r) / (uint32_t)ps) : ibase + rel0 + r;
     __builtin_amdgcn_global_load_lds((const void*)(indices + e), (MLA_LDS void*)(buf + Lds<true>::kIdx), 4, 0,
                                      0);
   }
@@ -201,16 +204,17 @@ __device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restric
 // row's 18 scale bytes come as the two aligned 16-byte chunks that cover
 // them (an 18-byte row starts at an even offset, so two always suffice)
 // into the row's 32-byte slot. All indices are read before any load is
-// issued. With pages (ps > 1) the slot first has its page numbers turned
+// issued. With pages (kPages) the slot first has its page numbers turned
 // into pool rows, page * ps + the row's offset in its page, for every later
 // reader of the slot.
+template <bool kPages>
 __device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __restrict__ kv,
                                              const uint8_t* __restrict__ sc, int rel0, int nvalid, int ps,
                                              int lane) {
   rel0 = __builtin_amdgcn_readfirstlane(rel0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   const int last = min(nvalid, kTile) - 1;
-  if (ps != 1 && lane < kTile) {
+  if (kPages && lane < kTile) {
     int32_t* slot = (int32_t*)(buf + Lds<true>::kIdx);
     const uint32_t in_page = (uint32_t)(rel0 + min(lane, last)) % (uint32_t)ps;
     slot[lane] = (int32_t)((uint32_t)slot[lane] * (uint32_t)ps + in_page);
@@ -629,7 +633,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
   pv_block<0>(tra, sca, v_cur, s_lo, s_hi, pa, o);
 }
 
-template <bool kGather>
+template <bool kGather, bool kPages>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
@@ -667,7 +671,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int ke = min(items[4 * it + 2], seq_hi);
       const int dest = items[4 * it + 3];
       // first entry of the sequence in kv_indices: its page list, or its rows
-      const int ibase = kGather && page_indptr != nullptr ? page_indptr[b] : seq_lo;
+      const int ibase = kPages ? page_indptr[b] : seq_lo;
 
       const int len = ke - kb;
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
@@ -693,12 +697,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         if (ntiles > 0) {
           if constexpr (kGather) {
             // row indices of the first two tiles, then tile 0 from them
-            stage_idx(ring, kv_indices, ibase, t_first - seq_lo, ke - t_first, page_size, lane);
+            stage_idx<kPages>(ring, kv_indices, ibase, t_first - seq_lo, ke - t_first, page_size, lane);
             if (ntiles > 1)
-              stage_idx(ring + L::kBuf, kv_indices, ibase, t_first + kTileStride - seq_lo,
+              stage_idx<kPages>(ring + L::kBuf, kv_indices, ibase, t_first + kTileStride - seq_lo,
                         ke - t_first - kTileStride, page_size, lane);
             wait_dma();
-            stage_gather(ring, kv, sc, t_first - seq_lo, ke - t_first, page_size, lane);
+            stage_gather<kPages>(ring, kv, sc, t_first - seq_lo, ke - t_first, page_size, lane);
           } else {
             stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
           }
@@ -713,9 +717,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
               // tile i + 1 from the indices staged a round ago; the indices
               // of tile i + 2 go to the slot of the buffer it will use (the
               // P V wave reads only that buffer's rows this round)
-              stage_gather(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn - seq_lo, ke - tn, page_size, lane);
+              stage_gather<kPages>(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn - seq_lo, ke - tn, page_size, lane);
               if (i + 2 < ntiles)
-                stage_idx(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, ibase, tn + kTileStride - seq_lo,
+                stage_idx<kPages>(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, ibase, tn + kTileStride - seq_lo,
                           ke - tn - kTileStride, page_size, lane);
             } else {
               stage_dma(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn, ke - tn, lane);
@@ -963,12 +967,18 @@ size_t decode_lds_bytes() { return (size_t)Lds<true>::kTotal; }
 int launch_decode(const DecodeArgs& a, void* stream) {
   if (a.num_slots <= 0 || a.grid <= 0) return (int)hipSuccess;
   if (a.kv_indices != nullptr) {
-    hipLaunchKernelGGL(mla_decode_kernel<true>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, a.kv_indices,
-                       a.page_indptr, a.page_size, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
-                       a.score_scale_log2);
+    if (a.page_indptr != nullptr)
+      hipLaunchKernelGGL((mla_decode_kernel<true, true>), dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
+                         (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, a.kv_indices,
+                         a.page_indptr, a.page_size, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
+                         a.score_scale_log2);
+    else
+      hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(a.grid), dim3(kThreads), 0,
+                         (hipStream_t)stream, (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr,
+                         a.kv_indices, (const int32_t*)nullptr, 1, (uint16_t*)a.out, a.plan, a.part_lse,
+                         a.part_out, a.score_scale_log2);
   } else {
-    hipLaunchKernelGGL(mla_decode_kernel<false>, dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (const int32_t*)nullptr,
                        (const int32_t*)nullptr, 1, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
                        a.score_scale_log2);
