@@ -176,26 +176,45 @@ __device__ __forceinline__ void stage_dma(uint8_t* buf, const uint8_t* __restric
   stage_dma<0, kRowDma, true>(buf, kv, sc, t0, nvalid, lane);
 }
 
-// Row indices of a tile into the buffer's index slot, one 4-byte direct
-// load per lane of the first 32. The tile starts `rel0` tokens into its
-// sequence, whose entries in `indices` start at `ibase`; tile row r (the
-// last valid one repeated past the item's end) takes entry
-// ibase + (rel0 + r) / ps, its page. A per-token row list is ps = 1 with
-// ibase = the sequence's first token, so the entry is the token's own row.
-// kPages selects the page-table form at compile time (the row-list kernel
-// then carries none of the page arithmetic).
-template <bool kPages>
-__device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restrict__ indices, int ibase,
-                                          int rel0, int nvalid, int ps, int lane) {
-  ibase = __builtin_amdgcn_readfirstlane(ibase);
-  rel0 = __builtin_amdgcn_readfirstlane(rel0);
+// Row indices of the tile starting at token t0 (kv_indices[t0 .. t0 + 31],
+// the last valid one repeated past the item's end) into the buffer's index
+// slot: one 4-byte direct load per lane of the first 32.
+__device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restrict__ kv_indices, int t0,
+                                          int nvalid, int lane) {
+  t0 = __builtin_amdgcn_readfirstlane(t0);
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   if (lane < kTile) {
     const int r = min(lane, nvalid - 1);
-    const int e = kPages ? ibase + (int)((uint32_t)(rel0 + r) / (uint32_t)ps) : ibase + rel0 + r;
-    __builtin_amdgcn_global_load_lds((const void*)(indices + e), (MLA_LDS void*)(buf + Lds<true>::kIdx), 4, 0,
-                                     0);
+    __builtin_amdgcn_global_load_lds((const void*)(kv_indices + t0 + r),
+                                     (MLA_LDS void*)(buf + Lds<true>::kIdx), 4, 0, 0);
   }
+}
+
+// Page tables: the row of tile row r (lanes 0..31; the last valid row
+// repeated past the item's end) is page * ps + x % ps with x = rel0 + r its
+// token's position in the sequence and page = indices[ibase + x / ps]. The
+// page entries are loaded into registers a round before the rows are
+// needed, and stored as rows into the index slot just before the tile is
+// staged, so every later reader of the slot sees rows.
+struct PageRows {
+  uint32_t page;   // the token's page (in flight until the next round)
+  uint32_t off;    // its row within the page
+};
+
+__device__ __forceinline__ PageRows load_pages(const int32_t* __restrict__ indices, int ibase, int rel0,
+                                               int nvalid, int ps, int lane) {
+  rel0 = __builtin_amdgcn_readfirstlane(rel0);
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const uint32_t x = (uint32_t)(rel0 + min(min(lane, kTile - 1), nvalid - 1));
+  const uint32_t pg = x / (uint32_t)ps;
+  PageRows r;
+  r.off = x - pg * (uint32_t)ps;
+  r.page = (uint32_t)indices[ibase + (int)pg];
+  return r;
+}
+
+__device__ __forceinline__ void store_page_rows(uint8_t* buf, const PageRows& r, int ps, int lane) {
+  if (lane < kTile) ((int32_t*)(buf + Lds<true>::kIdx))[lane] = (int32_t)(r.page * (uint32_t)ps + r.off);
 }
 
 // Stage a tile whose rows are listed in the buffer's index slot: lane chunk
@@ -204,21 +223,11 @@ __device__ __forceinline__ void stage_idx(uint8_t* buf, const int32_t* __restric
 // row's 18 scale bytes come as the two aligned 16-byte chunks that cover
 // them (an 18-byte row starts at an even offset, so two always suffice)
 // into the row's 32-byte slot. All indices are read before any load is
-// issued. With pages (kPages) the slot first has its page numbers turned
-// into pool rows, page * ps + the row's offset in its page, for every later
-// reader of the slot.
-template <bool kPages>
+// issued.
 __device__ __forceinline__ void stage_gather(uint8_t* buf, const uint8_t* __restrict__ kv,
-                                             const uint8_t* __restrict__ sc, int rel0, int nvalid, int ps,
-                                             int lane) {
-  rel0 = __builtin_amdgcn_readfirstlane(rel0);
+                                             const uint8_t* __restrict__ sc, int nvalid, int lane) {
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   const int last = min(nvalid, kTile) - 1;
-  if (kPages && lane < kTile) {
-    int32_t* slot = (int32_t*)(buf + Lds<true>::kIdx);
-    const uint32_t in_page = (uint32_t)(rel0 + min(lane, last)) % (uint32_t)ps;
-    slot[lane] = (int32_t)((uint32_t)slot[lane] * (uint32_t)ps + in_page);
-  }
   const int32_t* idx = (const int32_t*)(buf + Lds<true>::kIdx);
   uint32_t off[kRowDma];
 #pragma unroll
@@ -671,7 +680,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int ke = min(items[4 * it + 2], seq_hi);
       const int dest = items[4 * it + 3];
       // first entry of the sequence in kv_indices: its page list, or its rows
-      const int ibase = kPages ? page_indptr[b] : seq_lo;
+      const int ibase = kPages ? page_indptr[b] : 0;   // the sequence's first page entry
 
       const int len = ke - kb;
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
@@ -693,16 +702,24 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
         st.m = kMInit;
         const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp);
+        PageRows pages = {0u, 0u};   // page tables: the entries of the next tile to stage
         __syncthreads();  // LDS of the previous item's merge is free again
         if (ntiles > 0) {
-          if constexpr (kGather) {
-            // row indices of the first two tiles, then tile 0 from them
-            stage_idx<kPages>(ring, kv_indices, ibase, t_first - seq_lo, ke - t_first, page_size, lane);
+          if constexpr (kPages) {
+            // rows of tile 0, then its staging; the pages of tile 1 fly
+            store_page_rows(ring, load_pages(kv_indices, ibase, t_first - seq_lo, ke - t_first, page_size, lane),
+                            page_size, lane);
             if (ntiles > 1)
-              stage_idx<kPages>(ring + L::kBuf, kv_indices, ibase, t_first + kTileStride - seq_lo,
-                        ke - t_first - kTileStride, page_size, lane);
+              pages = load_pages(kv_indices, ibase, t_first + kTileStride - seq_lo, ke - t_first - kTileStride,
+                                 page_size, lane);
+            stage_gather(ring, kv, sc, ke - t_first, lane);
+          } else if constexpr (kGather) {
+            // row indices of the first two tiles, then tile 0 from them
+            stage_idx(ring, kv_indices, t_first, ke - t_first, lane);
+            if (ntiles > 1)
+              stage_idx(ring + L::kBuf, kv_indices, t_first + kTileStride, ke - t_first - kTileStride, lane);
             wait_dma();
-            stage_gather<kPages>(ring, kv, sc, t_first - seq_lo, ke - t_first, page_size, lane);
+            stage_gather(ring, kv, sc, ke - t_first, lane);
           } else {
             stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
           }
@@ -713,14 +730,23 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           __syncthreads();  // tile i landed; tile i-2 fully consumed; hand-off of i-1 visible
           if (i + 1 < ntiles) {
             const int tn = t_first + (i + 1) * kTileStride;
-            if constexpr (kGather) {
+            if constexpr (kPages) {
+              // tile i + 1's rows from the pages loaded a round ago (the
+              // round's wait above drained them too), then the pages of i + 2
+              uint8_t* bn = ring + ((i + 1) % kNumBuf) * L::kBuf;
+              store_page_rows(bn, pages, page_size, lane);
+              stage_gather(bn, kv, sc, ke - tn, lane);
+              if (i + 2 < ntiles)
+                pages = load_pages(kv_indices, ibase, tn + kTileStride - seq_lo, ke - tn - kTileStride, page_size,
+                                   lane);
+            } else if constexpr (kGather) {
               // tile i + 1 from the indices staged a round ago; the indices
               // of tile i + 2 go to the slot of the buffer it will use (the
               // P V wave reads only that buffer's rows this round)
-              stage_gather<kPages>(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn - seq_lo, ke - tn, page_size, lane);
+              stage_gather(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, ke - tn, lane);
               if (i + 2 < ntiles)
-                stage_idx<kPages>(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, ibase, tn + kTileStride - seq_lo,
-                          ke - tn - kTileStride, page_size, lane);
+                stage_idx(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, tn + kTileStride,
+                          ke - tn - kTileStride, lane);
             } else {
               stage_dma(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn, ke - tn, lane);
             }
