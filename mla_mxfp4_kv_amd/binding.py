@@ -501,6 +501,19 @@ class MlaDecodeDevicePlan:
             raise ValueError(f"unknown cache format {fmt!r}")
         return out
 
+    def decode_page_table(self, fmt, q, pool, kv_scale, page_indices, page_indptr, page_size: int, kv_indptr,
+                          out, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        """Page-table decode on the device plan (``kv_indptr``: the device
+        token offsets the plan was built from; ``page_indptr``: the device
+        page offsets). Nothing is checked (the tables may change on the
+        device between graph replays): the caller keeps them consistent."""
+        _validate_qo(q, out, self.batch)
+        if fmt not in ("mxfp4", "fp8", "bf16"):
+            raise ValueError(f"unknown cache format {fmt!r}")
+        decode_page_table(fmt, q, pool, kv_scale, page_indices, page_indptr, page_size, kv_indptr, out, sm_scale,
+                          self.workspace, stream)
+        return out
+
     def decode_fp8(self, q, kv_fp8, kv_scale, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0),
                    stream=None):
         """fp8-cache decode on the device plan (kv_fp8 uint8 [T,576], kv_scale float32 [1])."""

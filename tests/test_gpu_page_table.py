@@ -254,3 +254,79 @@ def test_page_table_errors():
     assert L.mla_decode_mxfp4_page_table(*args[:3], None, ptr(dec.page_indptr), ps, *tail) == -1
     assert L.mla_decode_mxfp4_page_table(*args, ptr(dec.page_indptr), ps, *tail) == 0
     torch.cuda.synchronize()
+
+
+def test_growing_page_table_replayed_in_a_graph():
+    """A serving loop: the GPU-side plan and the page-table decode captured
+    once in a HIP graph, then replayed while every sequence grows by one
+    token per step (crossing page boundaries, new pages taken from a free
+    list) and the tables are rewritten in place between replays. Each
+    replay equals the eager decode of the same state through a host plan."""
+    _say("case page table growing in a graph")
+    ps, batch, steps = 16, 4, 6
+    start = [15, 31, 1, 40]            # sequences 0 and 1 cross a page boundary on step 1
+    max_tokens = sum(start) + batch * steps
+    slots = 64
+    rng = np.random.default_rng(11)
+    pool_p = torch.from_numpy(rng.integers(0, 256, (slots * ps, 288), dtype=np.uint8)).cuda()
+    # scales 2^-5..2^0 keep the scores of random codes moderate (larger ones
+    # make softmax pick single tokens, where the tolerance is too tight)
+    pool_s = torch.from_numpy(rng.integers(122, 128, (slots * ps, 18), dtype=np.uint8)).cuda()
+    free = list(rng.permutation(slots))
+    owned = [[] for _ in range(batch)]
+
+    def tables(lens):
+        for b, n in enumerate(lens):
+            while len(owned[b]) * ps < n:
+                owned[b].append(int(free.pop()))
+        pi = np.concatenate([[0], np.cumsum([len(o) for o in owned])])
+        last = [n - (len(o) - 1) * ps for n, o in zip(lens, owned)]
+        pages = np.concatenate([np.array(o, dtype=np.int32) for o in owned])
+        return pi, last, pages
+
+    q = torch.randn(batch, 16, 576, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    max_pages = (max_tokens + batch * ps) // ps
+    dev = binding.MlaDecodeDevicePlan(batch, max_tokens, device="cuda", num_cus=6)
+    d_pages = torch.zeros(max_pages, dtype=torch.int32, device="cuda")
+    d_pi = torch.zeros(batch + 1, dtype=torch.int32, device="cuda")
+    d_tok = torch.zeros(batch + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty(batch, 16, 512, dtype=torch.bfloat16, device="cuda")
+
+    def upload(lens):
+        pi, last, pages = tables(lens)
+        d_pages[: len(pages)].copy_(torch.from_numpy(pages))
+        d_pi.copy_(torch.from_numpy(pi.astype(np.int32)))
+        tok = binding.page_table_kv_indptr(pi.tolist(), last, ps)
+        d_tok.copy_(torch.tensor(tok, dtype=torch.int32))
+        torch.cuda.synchronize()
+        return pi, last
+
+    lens = list(start)
+    upload(lens)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        dev.plan(d_tok, stream=s)
+        dev.decode_page_table("mxfp4", q, pool_p, pool_s, d_pages, d_pi, ps, d_tok, out, sm_scale=SM, stream=s)
+        s.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            dev.plan(d_tok, stream=s)
+            dev.decode_page_table("mxfp4", q, pool_p, pool_s, d_pages, d_pi, ps, d_tok, out, sm_scale=SM,
+                                  stream=s)
+    torch.cuda.synchronize()
+    for step in range(steps):
+        lens = [n + 1 for n in lens]
+        pi, last = upload(lens)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        host = binding.MlaDecodePageTable(pi.tolist(), last, ps, device="cuda", num_cus=6)
+        want = host.mxfp4(q, pool_p, pool_s, d_pages[: int(pi[-1])].contiguous(), sm_scale=SM)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"step {step}"
+    # the last state against the oracle
+    exp = ref.mla_decode_ref_page_table(_qbits(q), pool_p.cpu().numpy(), pool_s.cpu().numpy(),
+                                        d_pages[: int(pi[-1])].cpu().numpy(), pi, last, ps, SM)
+    _check(out.float().cpu().numpy(), exp, "growing page table, last step")
