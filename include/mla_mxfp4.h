@@ -217,6 +217,30 @@ int mla_decode_bf16_paged(const void* q, const void* kv_bf16, const int32_t* kv_
                           const int32_t* kv_indptr, void* out, float sm_scale,
                           void* workspace, void* stream);
 
+/* The three decodes over contiguous rows that sequences may share: sequence
+ * b reads rows kv_start[b] .. kv_start[b] + (kv_indptr[b+1] - kv_indptr[b])
+ * - 1 of the cache (kv_start: int32 [B] on the device, 4-byte aligned),
+ * while kv_indptr (the offsets the plan was built from) only gives the
+ * lengths and the order of work. Several query entries can then attend the
+ * same rows. Page "kernelbot-amd-mixed-mla-676098" runs q_seq_len query
+ * tokens per sequence in its Triton decode, query token i over the whole
+ * KV range of sequence i / q_seq_len. A 128-head query (the H = 128
+ * configuration named on the same page) is eight 16-head groups over the
+ * same rows. Each entry is a full 16-head decode and reads its rows
+ * itself. The caller guarantees that every row read lies inside the cache
+ * (the Python binding checks it). Pools, q, out and everything else as
+ * for the plain decodes of each format; MLA_ERR_INVALID for a null or
+ * misaligned kv_start. */
+int mla_decode_mxfp4_starts(const void* q, const void* kv_packed, const void* kv_scale,
+                            const int32_t* kv_start, const int32_t* kv_indptr, void* out,
+                            float sm_scale, void* workspace, void* stream);
+int mla_decode_fp8_starts(const void* q, const void* kv_fp8, const float* kv_scale,
+                          const int32_t* kv_start, const int32_t* kv_indptr, void* out,
+                          float sm_scale, void* workspace, void* stream);
+int mla_decode_bf16_starts(const void* q, const void* kv_bf16, const int32_t* kv_start,
+                           const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
+                           void* stream);
+
 /* The three decodes over a page table (page "kernelbot-amd-mixed-mla-676098",
  * _aiter_mla_decode, passes kv_indptr, kv_indices, kv_last_page_len and
  * page_size to its decode; page_size is 1 there). Sequence b owns pages

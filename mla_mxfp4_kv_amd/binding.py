@@ -28,7 +28,7 @@ EXPORTS = (
     "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
     "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
     "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
-    "mla_decode_bf16_page_table",
+    "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts", "mla_decode_bf16_starts",
 )
 
 _lib = None
@@ -80,11 +80,17 @@ def lib():
     L.mla_decode_mxfp4_page_table.argtypes = pt
     L.mla_decode_fp8_page_table.argtypes = pt
     L.mla_decode_bf16_page_table.argtypes = pt[:1] + pt[2:]
+    # (q, pool, [scale,] kv_start, kv_indptr, out, sm_scale, workspace, stream)
+    st = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_mxfp4_starts.argtypes = st
+    L.mla_decode_fp8_starts.argtypes = st
+    L.mla_decode_bf16_starts.argtypes = st[:1] + st[2:]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
                  "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
                  "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
                  "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
-                 "mla_decode_bf16_page_table"):
+                 "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts",
+                 "mla_decode_bf16_starts"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -228,6 +234,19 @@ def decode_page_table(fmt: str, q, pool, kv_scale, page_indices, page_indptr_dev
         *head, ctypes.c_void_p(page_indices.data_ptr()), ctypes.c_void_p(page_indptr_dev.data_ptr()),
         ctypes.c_int32(page_size), ctypes.c_void_p(kv_indptr_dev.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), fn)
+
+
+def decode_starts(fmt: str, q, pool, kv_scale, kv_start_dev, kv_indptr_dev, out, sm_scale: float, workspace,
+                  stream=None):
+    """Enqueue a decode over shared contiguous rows (no checks; see ``MlaDecodeGroups``)."""
+    head = [ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(pool.data_ptr())]
+    if fmt != "bf16":
+        head.append(ctypes.c_void_p(kv_scale.data_ptr()))
+    fn = f"mla_decode_{fmt}_starts"
+    _check(getattr(lib(), fn)(
+        *head, ctypes.c_void_p(kv_start_dev.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()),
+        _stream_ptr(stream)), fn)
 
 
 def page_table_kv_indptr(page_indptr, kv_last_page_len, page_size: int):
@@ -452,6 +471,74 @@ class MlaDecodePageTable:
              check=True):
         """bf16 decode: kv_bf16 bfloat16 [R,576]."""
         return self._run("bf16", q, kv_bf16, None, page_indices, out, sm_scale, stream, check, 2 * QK_DIM)
+
+
+class MlaDecodeGroups:
+    """A planned decode where every sequence of a contiguous cache serves
+    ``groups`` consecutive 16-head query entries: entry e = b * groups + g
+    reads the rows of sequence b (``kv_indptr`` on the host, as for
+    ``MlaDecode``). q is bf16 [B * groups, 16, 576] and out bf16
+    [B * groups, 16, 512]:
+    * q_seq_len query tokens per sequence (token j of sequence b is entry
+      b * q_seq_len + j): groups = q_seq_len;
+    * 128 heads: q [B, 128, 576] viewed as [B * 8, 16, 576], groups = 8
+      (both: groups = 8 * q_seq_len).
+    Each entry is a full 16-head decode that reads the sequence's rows."""
+
+    def __init__(self, kv_indptr, groups: int, device="cuda", num_cus: int = 0):
+        import torch
+        ind = [int(v) for v in kv_indptr]
+        if groups < 1:
+            raise ValueError("groups must be >= 1")
+        self.groups = int(groups)
+        self.indptr_host = ind
+        lens = [b - a for a, b in zip(ind, ind[1:])]
+        entry = [0]
+        for n in lens:
+            for _ in range(self.groups):
+                entry.append(entry[-1] + n)
+        if entry[-1] >= 2 ** 31:
+            raise ValueError("more than 2^31 - 1 tokens over all entries")
+        self.plan = MlaDecode(entry, device=device, num_cus=num_cus)
+        self.batch = self.plan.batch
+        self.device = self.plan.device
+        self.kv_indptr = self.plan.kv_indptr
+        starts = [ind[e // self.groups] for e in range(self.batch)]
+        self.kv_start = torch.tensor(starts if starts else [0], dtype=torch.int32, device=self.device)
+
+    def _run(self, fmt, q, pool, kv_scale, out, sm_scale, stream):
+        import torch
+        # [B, 16 * g, 576] (e.g. 128 heads) and [B * g, 16, 576] are the same memory
+        if q.is_contiguous() and q.numel() == self.batch * NUM_HEADS * QK_DIM:
+            q = q.view(self.batch, NUM_HEADS, QK_DIM)
+        if out is not None and out.is_contiguous() and out.numel() == self.batch * NUM_HEADS * V_DIM:
+            out = out.view(self.batch, NUM_HEADS, V_DIM)
+        out = self.plan._out(q, out)
+        if fmt == "mxfp4":
+            _validate(q, pool, kv_scale, out, self.batch)
+        elif fmt == "fp8":
+            if pool.dtype not in (torch.uint8, torch.float8_e4m3fn) or pool.dim() != 2 \
+                    or pool.shape[1] != QK_DIM or not pool.is_contiguous():
+                raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [T,576]")
+            if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != pool.device:
+                raise ValueError("kv_scale must be a float32 device tensor of one element")
+        elif pool.dtype != torch.bfloat16 or pool.dim() != 2 or pool.shape[1] != QK_DIM \
+                or not pool.is_contiguous():
+            raise ValueError("kv_bf16 must be contiguous bfloat16 [T,576]")
+        if pool.shape[0] < self.indptr_host[-1]:
+            raise ValueError("kv_indptr reaches past the end of the cache rows")
+        decode_starts(fmt, q, pool, kv_scale, self.kv_start, self.kv_indptr, out, sm_scale, self.plan.workspace,
+                      stream)
+        return out
+
+    def mxfp4(self, q, kv_packed, kv_scale, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        return self._run("mxfp4", q, kv_packed, kv_scale, out, sm_scale, stream)
+
+    def fp8(self, q, kv_fp8, kv_scale, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        return self._run("fp8", q, kv_fp8, kv_scale, out, sm_scale, stream)
+
+    def bf16(self, q, kv_bf16, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        return self._run("bf16", q, kv_bf16, None, out, sm_scale, stream)
 
 
 class MlaDecodeDevicePlan:

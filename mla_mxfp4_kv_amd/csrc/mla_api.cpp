@@ -215,7 +215,8 @@ enum class KvFormat { kMxfp4, kFp8, kBf16 };
 int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_scale,
                   const int32_t* kv_indices, const int32_t* kv_indptr, void* out, float sm_scale,
                   void* workspace, void* stream, bool gather = false,
-                  const int32_t* page_indptr = nullptr, int32_t page_size = 1) {
+                  const int32_t* page_indptr = nullptr, int32_t page_size = 1,
+                  const int32_t* kv_start = nullptr) {
   int dev;
   DeviceInfo info;
   int st = current_device(&dev, &info);
@@ -260,6 +261,7 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   a.kv_indices = gather ? kv_indices : nullptr;
   a.page_indptr = gather ? page_indptr : nullptr;
   a.page_size = gather ? page_size : 1;
+  a.kv_start = gather ? nullptr : kv_start;
   a.out = out;
   a.plan = (const int32_t*)workspace;
   a.part_lse = (float*)((uint8_t*)workspace + pe.off_lse);
@@ -281,6 +283,15 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   e = (hipError_t)mla::launch_reduce(a, stream);
   if (e != hipSuccess) return hip_fail(e, "mla_reduce_kernel launch");
   return MLA_OK;
+}
+
+// A shared-rows call needs its start rows.
+bool starts_ok(const int32_t* kv_start) {
+  if (kv_start == nullptr || !aligned(kv_start, 4)) {
+    fail(MLA_ERR_INVALID, "kv_start must be a non-null 4-byte aligned device pointer");
+    return false;
+  }
+  return true;
 }
 
 // A page-table call needs its page offsets (checked before the plan, so an
@@ -349,6 +360,27 @@ int mla_decode_fp8_page_table(const void* q, const void* kv_fp8, const float* kv
   if (!page_table_ok(page_indptr)) return MLA_ERR_INVALID;
   return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, page_indices, kv_indptr, out, sm_scale, workspace,
                        stream, true, page_indptr, page_size);
+}
+
+int mla_decode_mxfp4_starts(const void* q, const void* kv_packed, const void* kv_scale, const int32_t* kv_start,
+                            const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
+  if (!starts_ok(kv_start)) return MLA_ERR_INVALID;
+  return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, nullptr, kv_indptr, out, sm_scale, workspace,
+                       stream, false, nullptr, 1, kv_start);
+}
+
+int mla_decode_fp8_starts(const void* q, const void* kv_fp8, const float* kv_scale, const int32_t* kv_start,
+                          const int32_t* kv_indptr, void* out, float sm_scale, void* workspace, void* stream) {
+  if (!starts_ok(kv_start)) return MLA_ERR_INVALID;
+  return decode_common(KvFormat::kFp8, q, kv_fp8, kv_scale, nullptr, kv_indptr, out, sm_scale, workspace, stream,
+                       false, nullptr, 1, kv_start);
+}
+
+int mla_decode_bf16_starts(const void* q, const void* kv_bf16, const int32_t* kv_start, const int32_t* kv_indptr,
+                           void* out, float sm_scale, void* workspace, void* stream) {
+  if (!starts_ok(kv_start)) return MLA_ERR_INVALID;
+  return decode_common(KvFormat::kBf16, q, kv_bf16, nullptr, nullptr, kv_indptr, out, sm_scale, workspace, stream,
+                       false, nullptr, 1, kv_start);
 }
 
 int mla_decode_bf16_page_table(const void* q, const void* kv_bf16, const int32_t* page_indices,

@@ -488,8 +488,9 @@ __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                         const float* __restrict__ kv_scale, const int32_t* __restrict__ kv_indptr,
                         const int32_t* __restrict__ kv_indices, const int32_t* __restrict__ page_indptr,
-                        int page_size, uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
-                        float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
+                        int page_size, const int32_t* __restrict__ kv_start, uint16_t* __restrict__ out,
+                        const int32_t* __restrict__ plan, float* __restrict__ part_lse,
+                        float* __restrict__ part_out, float csc) {
   using C = Cfg<kFp8>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kGather ? kLdsGather : kLdsTotal];
   const int tid = threadIdx.x;
@@ -522,6 +523,9 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
       // first entry of the sequence in kv_indices: its page list, or its rows
       const int seq_lo = kv_indptr[b];
       const int ibase = kGather && page_indptr != nullptr ? page_indptr[b] : seq_lo;
+      // contiguous rows from kv_start[b] on, when given (shared by sequences)
+      const uint8_t* kv_b = kv;
+      if (!kGather && kv_start != nullptr) kv_b += ((ptrdiff_t)kv_start[b] - seq_lo) * C::kRow;
       const int t_first = kb + C::kTile * wave;
       const int ntiles = t_first < ke ? (ke - t_first + C::kStride - 1) / C::kStride : 0;
 
@@ -632,12 +636,12 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
           compute(ring + (i & 1) * kTileBytes, i);
         }
       } else {
-        if (ntiles > 0) stage_tile<kFp8>(ring, kv, t_first, ke - t_first, lane);
+        if (ntiles > 0) stage_tile<kFp8>(ring, kv_b, t_first, ke - t_first, lane);
         for (int i = 0; i < ntiles; ++i) {
           // tile i + 1 goes into the other buffer before tile i is waited for
           if (i + 1 < ntiles) {
             const int tn = t_first + (i + 1) * C::kStride;
-            stage_tile<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv, tn, ke - tn, lane);
+            stage_tile<kFp8>(ring + ((i + 1) & 1) * kTileBytes, kv_b, tn, ke - tn, lane);
             wait_vm<kDma>();
           } else {
             wait_vm<0>();
@@ -719,7 +723,8 @@ static void launch_dense(const DecodeArgs& a, const float* kv_scale, void* strea
   hipLaunchKernelGGL((mla_decode_dense_kernel<kFp8, kGather>), dim3(a.grid), dim3(kThreads), 0,
                      (hipStream_t)stream, (const uint16_t*)a.q, a.kv_packed, kv_scale, a.kv_indptr, a.kv_indices,
                      kGather ? a.page_indptr : (const int32_t*)nullptr, kGather ? a.page_size : 1,
-                     (uint16_t*)a.out, a.plan, a.part_lse, a.part_out, a.score_scale_log2);
+                     kGather ? (const int32_t*)nullptr : a.kv_start, (uint16_t*)a.out, a.plan, a.part_lse,
+                     a.part_out, a.score_scale_log2);
 }
 
 int launch_decode_dense(const DecodeArgs& a, bool fp8, const float* kv_scale, void* stream) {

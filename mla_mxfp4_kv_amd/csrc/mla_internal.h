@@ -70,6 +70,8 @@ struct DecodeArgs {
   const int32_t* page_indptr;  // with pages: sequence b's pages start at kv_indices[page_indptr[b]]
                                // (nullptr: kv_indices lists one row per token)
   int32_t page_size;           // rows per page (1 for a per-token row list)
+  const int32_t* kv_start;     // contiguous rows: sequence b starts at row kv_start[b]
+                               // (nullptr: at kv_indptr[b])
   void* out;
   const int32_t* plan;    // device plan words (workspace start)
   float* part_lse;

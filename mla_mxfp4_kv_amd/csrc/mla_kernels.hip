@@ -647,8 +647,9 @@ __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
                   const int32_t* __restrict__ kv_indices, const int32_t* __restrict__ page_indptr,
-                  int page_size, uint16_t* __restrict__ out, const int32_t* __restrict__ plan,
-                  float* __restrict__ part_lse, float* __restrict__ part_out, float csc) {
+                  int page_size, const int32_t* __restrict__ kv_start, uint16_t* __restrict__ out,
+                  const int32_t* __restrict__ plan, float* __restrict__ part_lse, float* __restrict__ part_out,
+                  float csc) {
   using L = Lds<kGather>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::kTotal];
   const int tid = threadIdx.x;
@@ -681,6 +682,16 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int dest = items[4 * it + 3];
       // first entry of the sequence in kv_indices: its page list, or its rows
       const int ibase = kPages ? page_indptr[b] : 0;   // the sequence's first page entry
+      // contiguous rows: with kv_start the sequence's tokens are the rows from
+      // kv_start[b] on (several sequences may share them); the tile code
+      // keeps kv_indptr positions and reads through shifted bases
+      const uint8_t* kv_b = kv;
+      const uint8_t* sc_b = sc;
+      if (!kGather && kv_start != nullptr) {
+        const ptrdiff_t shift = (ptrdiff_t)kv_start[b] - seq_lo;
+        kv_b += shift * kRowBytes;
+        sc_b += shift * kBlocks;
+      }
 
       const int len = ke - kb;
       const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
@@ -721,7 +732,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
             wait_dma();
             stage_gather(ring, kv, sc, ke - t_first, lane);
           } else {
-            stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
+            stage_dma(ring, kv_b, sc_b, t_first, ke - t_first, lane);
           }
         }
         for (int i = 0; i <= rounds; ++i) {
@@ -748,13 +759,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
                 stage_idx(ring + ((i + 2) % kNumBuf) * L::kBuf, kv_indices, tn + kTileStride,
                           ke - tn - kTileStride, lane);
             } else {
-              stage_dma(ring + ((i + 1) % kNumBuf) * L::kBuf, kv, sc, tn, ke - tn, lane);
+              stage_dma(ring + ((i + 1) % kNumBuf) * L::kBuf, kv_b, sc_b, tn, ke - tn, lane);
             }
           }
           if (qk_on) {
             const int tq = t_first + i * kTileStride;
             const uint8_t* bq = ring + (i % kNumBuf) * L::kBuf;
-            const int dq = kGather ? (int)((uintptr_t)sc & 15) : raw_delta(sc, tq);
+            const int dq = kGather ? (int)((uintptr_t)sc & 15) : raw_delta(sc_b, tq);
             const f32x4_t s0 = qk_subtile<kGather>(bq, dq, 0, qo, lane);
             const f32x4_t s1 = qk_subtile<kGather>(bq, dq, 1, qo, lane);
             hand[(i & 1) * (kPairs * 64)] = softmax_tile(s0, s1, tq, ke, st, csc, lane);
@@ -996,18 +1007,18 @@ int launch_decode(const DecodeArgs& a, void* stream) {
     if (a.page_indptr != nullptr)
       hipLaunchKernelGGL((mla_decode_kernel<true, true>), dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
                          (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, a.kv_indices,
-                         a.page_indptr, a.page_size, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
-                         a.score_scale_log2);
+                         a.page_indptr, a.page_size, (const int32_t*)nullptr, (uint16_t*)a.out, a.plan,
+                         a.part_lse, a.part_out, a.score_scale_log2);
     else
       hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(a.grid), dim3(kThreads), 0,
                          (hipStream_t)stream, (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr,
-                         a.kv_indices, (const int32_t*)nullptr, 1, (uint16_t*)a.out, a.plan, a.part_lse,
-                         a.part_out, a.score_scale_log2);
+                         a.kv_indices, (const int32_t*)nullptr, 1, (const int32_t*)nullptr, (uint16_t*)a.out,
+                         a.plan, a.part_lse, a.part_out, a.score_scale_log2);
   } else {
     hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (const int32_t*)nullptr,
-                       (const int32_t*)nullptr, 1, (uint16_t*)a.out, a.plan, a.part_lse, a.part_out,
-                       a.score_scale_log2);
+                       (const int32_t*)nullptr, 1, a.kv_start, (uint16_t*)a.out, a.plan, a.part_lse,
+                       a.part_out, a.score_scale_log2);
   }
   return (int)hipGetLastError();
 }

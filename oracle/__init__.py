@@ -48,6 +48,7 @@ from .mxfp4_ref import (  # noqa: F401
     mla_decode_ref_seq,
     mla_decode_ref_gather,
     mla_decode_ref_page_table,
+    mla_decode_ref_groups,
 )
 from .dense_ref import (  # noqa: F401
     E4M3_VALUES,
@@ -62,6 +63,8 @@ from .dense_ref import (  # noqa: F401
     mla_decode_ref_bf16_seq,
     mla_decode_ref_fp8_page_table,
     mla_decode_ref_bf16_page_table,
+    mla_decode_ref_fp8_groups,
+    mla_decode_ref_bf16_groups,
 )
 from .paging_ref import page_table_rows, page_table_token_indptr  # noqa: F401
 from .planner_ref import plan_words_ref, PlanRef, decode_plan_words  # noqa: F401

@@ -149,3 +149,26 @@ def mla_decode_ref_bf16_page_table(q, bits, page_indices, page_indptr, kv_last_p
     """bf16 oracle over a page table: float64 [B, 16, 512]."""
     return _page_table(lambda qb, r: mla_decode_ref_bf16_seq(qb, np.asarray(bits)[r], sm_scale),
                        q, page_indices, page_indptr, kv_last_page_len, page_size, batches)
+
+
+def _groups(fn, q, kv_indptr, groups, batches):
+    indptr = np.asarray(kv_indptr, dtype=np.int64)
+    q = np.asarray(q)
+    out = np.full((q.shape[0], NUM_HEADS, V_DIM), np.nan, dtype=np.float64)
+    for e in (range(q.shape[0]) if batches is None else batches):
+        b = e // groups
+        out[e] = fn(q[e], int(indptr[b]), int(indptr[b + 1]))
+    return out
+
+
+def mla_decode_ref_fp8_groups(q, codes, kv_scale, kv_indptr, groups: int, sm_scale: float, batches=None):
+    """fp8 oracle for query entries sharing their sequence's rows (entry e
+    reads sequence e // groups): float64 [E, 16, 512]."""
+    return _groups(lambda qb, lo, hi: mla_decode_ref_fp8_seq(qb, codes[lo:hi], kv_scale, sm_scale),
+                   q, kv_indptr, groups, batches)
+
+
+def mla_decode_ref_bf16_groups(q, bits, kv_indptr, groups: int, sm_scale: float, batches=None):
+    """bf16 oracle for query entries sharing their sequence's rows."""
+    return _groups(lambda qb, lo, hi: mla_decode_ref_bf16_seq(qb, bits[lo:hi], sm_scale),
+                   q, kv_indptr, groups, batches)

@@ -172,3 +172,20 @@ def mla_decode_ref_page_table(q, packed, scales, page_indices, page_indptr, kv_l
     for b in (range(len(rows)) if batches is None else batches):
         out[b] = mla_decode_ref_seq(q[b], np.asarray(packed)[rows[b]], np.asarray(scales)[rows[b]], sm_scale)
     return out
+
+
+def mla_decode_ref_groups(q, packed, scales, kv_indptr, groups: int, sm_scale: float,
+                          batches=None) -> np.ndarray:
+    """Query entries sharing their sequence's rows: entry e holds the 16
+    heads of query group e % groups of sequence e // groups (page
+    "kernelbot-amd-mixed-mla-676098": the Triton decode maps query token i
+    to sequence i // q_seq_len; a 128-head query is 8 such groups) and
+    attends all of that sequence's rows. float64 [E, 16, 512]."""
+    indptr = np.asarray(kv_indptr, dtype=np.int64)
+    q = np.asarray(q)
+    out = np.full((q.shape[0], NUM_HEADS, V_DIM), np.nan, dtype=np.float64)
+    for e in (range(q.shape[0]) if batches is None else batches):
+        b = e // groups
+        lo, hi = int(indptr[b]), int(indptr[b + 1])
+        out[e] = mla_decode_ref_seq(q[e], np.asarray(packed)[lo:hi], np.asarray(scales)[lo:hi], sm_scale)
+    return out
