@@ -174,6 +174,9 @@ def main(argv=None):
                     help="store every sequence in pages of PAGE rows (the last one partial), pages "
                          "shuffled over the pool (seeded), and decode through the page table (the "
                          "*_page_table entry points)")
+    ap.add_argument("--groups", type=int, default=0, metavar="G",
+                    help="G 16-head query entries per sequence over its shared rows (8: 128 heads; "
+                         "q_seq_len tokens: G = q_seq_len), the *_starts entry points")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
@@ -232,7 +235,22 @@ def main(argv=None):
                                  packed.shape[1] * packed.element_size())
         torch.cuda.synchronize()
     page_table = None
-    if args.page_table:
+    groups = None
+    if args.groups:
+        if args.gather or args.page_table:
+            print("--groups works on the contiguous cache only", file=sys.stderr)
+            return 2
+        groups = binding.MlaDecodeGroups(indptr.tolist(), args.groups, device=dev)
+        gq = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+        q = (torch.randn(groups.batch, 16, 576, generator=gq) * w.q_std).to(torch.bfloat16).to(dev)
+        out = torch.empty(groups.batch, 16, 512, dtype=torch.bfloat16, device=dev)
+        dec = groups.plan
+        words, _ = binding.plan_host(dec.indptr_host, binding.num_cus())
+
+        def call():
+            binding.decode_starts(fmt, q, packed, scales, groups.kv_start, dec.kv_indptr, out, w.sm_scale,
+                                  dec.workspace)
+    elif args.page_table:
         if args.gather:
             print("--gather and --page-table are exclusive", file=sys.stderr)
             return 2
@@ -342,7 +360,7 @@ def main(argv=None):
     achieved = alg / (avg_us * 1e-6) / 1e9
 
     cpu = None
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and not args.groups:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, q, packed, scales, lens, args.cpu_budget, fmt, kv_scale_host)
 
@@ -373,6 +391,7 @@ def main(argv=None):
             "kv_format": fmt,
             "gather_page_rows": args.gather or None,
             "page_table_rows": args.page_table or None,
+            "query_groups": args.groups or None,
             "batch": w.batch,
             "kv_len": w.kv_len if w.kv_len is not None else f"U{list(w.ragged)}",
             "total_tokens": total,
