@@ -187,8 +187,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures the single-GPU decode kernel; multi-GPU runs are not part "
-              "of this build (one GPU per box). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures the decode kernel on one GPU; runs over several GPUs are not "
+              "implemented (the decode would shard by sequence, see the design notes). Use --gpus 1.",
+              file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a HIP GPU", file=sys.stderr)
