@@ -512,7 +512,13 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
   f32x4_t* frag = (f32x4_t*)lds;
   float* stats = (float*)(lds + 2 * kHalfFrag);
 
-  for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
+  // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
+  // (kv_start), consecutive slots -- the query groups of one sequence --
+  // go to workgroups of one XCD, so that its L2 serves the repeated reads.
+  const bool xcd_order = !kGather && kv_start != nullptr && (gridDim.x & 7) == 0;
+  const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                   : (int)blockIdx.x;
+  for (int slot = first_slot; slot < num_slots; slot += gridDim.x) {
     const int i_begin = slot_indptr[slot];
     const int i_end = slot_indptr[slot + 1];
     for (int it = i_begin; it < i_end; ++it) {

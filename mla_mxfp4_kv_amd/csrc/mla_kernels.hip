@@ -670,7 +670,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // priority over the P V wave on the shared SIMD.
   if (scorer) __builtin_amdgcn_s_setprio(1);
 
-  for (int slot = blockIdx.x; slot < num_slots; slot += gridDim.x) {
+  // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
+  // (kv_start), consecutive slots -- the query groups of one sequence --
+  // go to workgroups of one XCD, so that its L2 serves the repeated reads.
+  const bool xcd_order = !kGather && kv_start != nullptr && (gridDim.x & 7) == 0;
+  const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                   : (int)blockIdx.x;
+  for (int slot = first_slot; slot < num_slots; slot += gridDim.x) {
     const int i_begin = slot_indptr[slot];
     const int i_end = slot_indptr[slot + 1];
     for (int it = i_begin; it < i_end; ++it) {
