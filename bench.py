@@ -30,11 +30,12 @@ KERNEL_SRC = {
     "fp8": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
     "bf16": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
 }
-KERNEL_NAME = {"mxfp4": "mla_decode_kernel<false, false>", "fp8": "mla_decode_dense_kernel<true, false>",
+KERNEL_NAME = {"mxfp4": "mla_decode_kernel<false, false, false>", "fp8": "mla_decode_dense_kernel<true, false>",
                "bf16": "mla_decode_dense_kernel<false, false>"}
-GATHER_KERNEL_NAME = {"mxfp4": "mla_decode_kernel<true, false>", "fp8": "mla_decode_dense_kernel<true, true>",
+GATHER_KERNEL_NAME = {"mxfp4": "mla_decode_kernel<true, false, false>", "fp8": "mla_decode_dense_kernel<true, true>",
                       "bf16": "mla_decode_dense_kernel<false, true>"}
-PAGE_TABLE_KERNEL_NAME = dict(GATHER_KERNEL_NAME, mxfp4="mla_decode_kernel<true, true>")
+PAGE_TABLE_KERNEL_NAME = dict(GATHER_KERNEL_NAME, mxfp4="mla_decode_kernel<true, true, false>")
+STARTS_KERNEL_NAME = dict(KERNEL_NAME, mxfp4="mla_decode_kernel<false, false, true>")
 
 
 def kernel_source_hash(fmt: str = "mxfp4") -> str:
@@ -409,9 +410,10 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if (args.gather or args.page_table) else measured_traffic(w.name, fmt),
+            "traffic": None if (args.gather or args.page_table or args.groups) else measured_traffic(w.name, fmt),
             "kernel": (PAGE_TABLE_KERNEL_NAME[fmt] if args.page_table
-                       else GATHER_KERNEL_NAME[fmt] if args.gather else KERNEL_NAME[fmt]),
+                       else GATHER_KERNEL_NAME[fmt] if args.gather
+                       else STARTS_KERNEL_NAME[fmt] if args.groups else KERNEL_NAME[fmt]),
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_source_sha256": kernel_source_hash(fmt),

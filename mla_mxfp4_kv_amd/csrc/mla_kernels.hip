@@ -642,7 +642,11 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
   pv_block<0>(tra, sca, v_cur, s_lo, s_hi, pa, o);
 }
 
-template <bool kGather, bool kPages>
+// kGather: rows listed through kv_indices (kPages: as a page table). kStarts
+// (contiguous rows only): sequence b starts at row kv_start[b], so that
+// several entries can share rows. Each mode is its own instantiation; the
+// plain contiguous kernel carries none of the others' code.
+template <bool kGather, bool kPages, bool kStarts = false>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
@@ -673,7 +677,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
   // (kv_start), consecutive slots -- the query groups of one sequence --
   // go to workgroups of one XCD, so that its L2 serves the repeated reads.
-  const bool xcd_order = !kGather && kv_start != nullptr && (gridDim.x & 7) == 0;
+  const bool xcd_order = kStarts && (gridDim.x & 7) == 0;
   const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
                                    : (int)blockIdx.x;
   for (int slot = first_slot; slot < num_slots; slot += gridDim.x) {
@@ -693,7 +697,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       // keeps kv_indptr positions and reads through shifted bases
       const uint8_t* kv_b = kv;
       const uint8_t* sc_b = sc;
-      if (!kGather && kv_start != nullptr) {
+      if (kStarts) {
         const ptrdiff_t shift = (ptrdiff_t)kv_start[b] - seq_lo;
         kv_b += shift * kRowBytes;
         sc_b += shift * kBlocks;
@@ -1021,10 +1025,16 @@ int launch_decode(const DecodeArgs& a, void* stream) {
                          a.kv_indices, (const int32_t*)nullptr, 1, (const int32_t*)nullptr, (uint16_t*)a.out,
                          a.plan, a.part_lse, a.part_out, a.score_scale_log2);
   } else {
-    hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (const int32_t*)nullptr,
-                       (const int32_t*)nullptr, 1, a.kv_start, (uint16_t*)a.out, a.plan, a.part_lse,
-                       a.part_out, a.score_scale_log2);
+    if (a.kv_start != nullptr)
+      hipLaunchKernelGGL((mla_decode_kernel<false, false, true>), dim3(a.grid), dim3(kThreads), 0,
+                         (hipStream_t)stream, (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr,
+                         (const int32_t*)nullptr, (const int32_t*)nullptr, 1, a.kv_start, (uint16_t*)a.out, a.plan,
+                         a.part_lse, a.part_out, a.score_scale_log2);
+    else
+      hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(a.grid), dim3(kThreads), 0, (hipStream_t)stream,
+                         (const uint16_t*)a.q, a.kv_packed, a.kv_scale, a.kv_indptr, (const int32_t*)nullptr,
+                         (const int32_t*)nullptr, 1, (const int32_t*)nullptr, (uint16_t*)a.out, a.plan,
+                         a.part_lse, a.part_out, a.score_scale_log2);
   }
   return (int)hipGetLastError();
 }
