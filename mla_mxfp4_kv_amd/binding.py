@@ -389,13 +389,8 @@ class MlaDecode:
     def fp8(self, q, kv_fp8, kv_scale, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
         """Decode over an fp8 cache: kv_fp8 uint8 E4M3 codes [T,576], kv_scale
         float32 [1] (per-tensor scale), both on the device."""
-        import torch
         out = self._out(q, out)
-        if kv_fp8.dtype not in (torch.uint8, torch.float8_e4m3fn) or kv_fp8.dim() != 2 \
-                or kv_fp8.shape[1] != QK_DIM or not kv_fp8.is_contiguous():
-            raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [T,576]")
-        if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != kv_fp8.device:
-            raise ValueError("kv_scale must be a float32 device tensor of one element")
+        _validate_dense("fp8", kv_fp8, kv_scale)
         if kv_fp8.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode_fp8(q, kv_fp8, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
@@ -403,11 +398,8 @@ class MlaDecode:
 
     def bf16(self, q, kv_bf16, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
         """Decode over a bf16 cache: kv_bf16 bfloat16 [T,576] on the device."""
-        import torch
         out = self._out(q, out)
-        if kv_bf16.dtype != torch.bfloat16 or kv_bf16.dim() != 2 or kv_bf16.shape[1] != QK_DIM \
-                or not kv_bf16.is_contiguous():
-            raise ValueError("kv_bf16 must be contiguous bfloat16 [T,576]")
+        _validate_dense("bf16", kv_bf16, None)
         if kv_bf16.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode_bf16(q, kv_bf16, self.kv_indptr, out, sm_scale, self.workspace, stream)
@@ -436,19 +428,11 @@ class MlaDecodePageTable:
         self.page_indptr = torch.tensor(self.page_indptr_host, dtype=torch.int32, device=self.device)
 
     def _run(self, fmt, q, pool, kv_scale, page_indices, out, sm_scale, stream, check, row_bytes):
-        import torch
         out = self.plan._out(q, out)
         if fmt == "mxfp4":
             _validate(q, pool, kv_scale, out, self.batch)
-        elif fmt == "fp8":
-            if pool.dtype not in (torch.uint8, torch.float8_e4m3fn) or pool.dim() != 2 \
-                    or pool.shape[1] != QK_DIM or not pool.is_contiguous():
-                raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [R,576]")
-            if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != pool.device:
-                raise ValueError("kv_scale must be a float32 device tensor of one element")
-        elif pool.dtype != torch.bfloat16 or pool.dim() != 2 or pool.shape[1] != QK_DIM \
-                or not pool.is_contiguous():
-            raise ValueError("kv_bf16 must be contiguous bfloat16 [R,576]")
+        else:
+            _validate_dense(fmt, pool, kv_scale)
         if check:
             check_page_table(page_indices, self.page_indptr_host, self.last_host, self.page_size,
                              pool.shape[0], row_bytes)
@@ -507,7 +491,6 @@ class MlaDecodeGroups:
         self.kv_start = torch.tensor(starts if starts else [0], dtype=torch.int32, device=self.device)
 
     def _run(self, fmt, q, pool, kv_scale, out, sm_scale, stream):
-        import torch
         # [B, 16 * g, 576] (e.g. 128 heads) and [B * g, 16, 576] are the same memory
         if q.is_contiguous() and q.numel() == self.batch * NUM_HEADS * QK_DIM:
             q = q.view(self.batch, NUM_HEADS, QK_DIM)
@@ -516,15 +499,8 @@ class MlaDecodeGroups:
         out = self.plan._out(q, out)
         if fmt == "mxfp4":
             _validate(q, pool, kv_scale, out, self.batch)
-        elif fmt == "fp8":
-            if pool.dtype not in (torch.uint8, torch.float8_e4m3fn) or pool.dim() != 2 \
-                    or pool.shape[1] != QK_DIM or not pool.is_contiguous():
-                raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [T,576]")
-            if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != pool.device:
-                raise ValueError("kv_scale must be a float32 device tensor of one element")
-        elif pool.dtype != torch.bfloat16 or pool.dim() != 2 or pool.shape[1] != QK_DIM \
-                or not pool.is_contiguous():
-            raise ValueError("kv_bf16 must be contiguous bfloat16 [T,576]")
+        else:
+            _validate_dense(fmt, pool, kv_scale)
         if pool.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode_starts(fmt, q, pool, kv_scale, self.kv_start, self.kv_indptr, out, sm_scale, self.plan.workspace,
@@ -621,6 +597,20 @@ def _validate_qo(q, out, batch):
         raise ValueError(f"q must be contiguous bf16 [{batch},16,576], got {q.dtype} {tuple(q.shape)}")
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (batch, NUM_HEADS, V_DIM) or not out.is_contiguous():
         raise ValueError("out must be contiguous bf16 [B,16,512]")
+
+
+def _validate_dense(fmt, pool, kv_scale):
+    """fp8: uint8 (or float8_e4m3fn) rows [R,576] and a one-element float32
+    scale on the same device; bf16: bfloat16 rows [R,576]."""
+    import torch
+    if fmt == "fp8":
+        if pool.dtype not in (torch.uint8, torch.float8_e4m3fn) or pool.dim() != 2 \
+                or pool.shape[1] != QK_DIM or not pool.is_contiguous():
+            raise ValueError("kv_fp8 must be contiguous uint8/float8_e4m3fn [rows,576]")
+        if kv_scale.dtype != torch.float32 or kv_scale.numel() != 1 or kv_scale.device != pool.device:
+            raise ValueError("kv_scale must be a float32 device tensor of one element")
+    elif pool.dtype != torch.bfloat16 or pool.dim() != 2 or pool.shape[1] != QK_DIM or not pool.is_contiguous():
+        raise ValueError("kv_bf16 must be contiguous bfloat16 [rows,576]")
 
 
 def _validate(q, kv_packed, kv_scale, out, batch):
