@@ -577,6 +577,18 @@ class MlaDecodeDevicePlan:
                           self.workspace, stream)
         return out
 
+    def decode_starts(self, fmt, q, pool, kv_scale, kv_start, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0),
+                      stream=None):
+        """Shared-row decode on the device plan: entry b reads its
+        ``kv_indptr`` length of rows from row ``kv_start[b]`` on (device
+        int32). Nothing is checked (the arrays may change on the device
+        between graph replays): the caller keeps the rows in the cache."""
+        _validate_qo(q, out, self.batch)
+        if fmt not in ("mxfp4", "fp8", "bf16"):
+            raise ValueError(f"unknown cache format {fmt!r}")
+        decode_starts(fmt, q, pool, kv_scale, kv_start, kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
     def decode_fp8(self, q, kv_fp8, kv_scale, kv_indptr, out, sm_scale=1.0 / math.sqrt(576.0),
                    stream=None):
         """fp8-cache decode on the device plan (kv_fp8 uint8 [T,576], kv_scale float32 [1])."""

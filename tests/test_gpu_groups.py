@@ -159,3 +159,63 @@ def test_groups_errors():
     assert L.mla_decode_mxfp4_starts(ptr(qd), ptr(pd), ptr(sd), ptr(dec.kv_start), ptr(dec.kv_indptr), ptr(out),
                                      SM, ptr(dec.plan.workspace), None) == 0
     torch.cuda.synchronize()
+
+
+def test_graph_replays_growing_query_groups():
+    """128 heads over sequences that grow by one token per step: the GPU-side
+    plan and the shared-row decode captured once in a HIP graph, replayed
+    with the offsets rewritten in place; every replay equals the eager
+    decode of the same state through a host plan."""
+    _say("case groups graph replay")
+    g, steps = 8, 4
+    start = [100, 1, 257]
+    total = sum(start) + len(start) * steps
+    q, cache, _, _ = _inputs("mxfp4", [total], g * len(start), seed=21)   # one cache, q for 3 x 8 entries
+    packed, scales = cache[0].cuda(), cache[1].cuda()
+    q = q.reshape(len(start) * g, 16, 576).cuda()
+    entries = len(start) * g
+    dev = binding.MlaDecodeDevicePlan(entries, total * g, device="cuda", num_cus=6)
+    d_start = torch.zeros(entries, dtype=torch.int32, device="cuda")
+    d_ind = torch.zeros(entries + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty(entries, 16, 512, dtype=torch.bfloat16, device="cuda")
+
+    def upload(lens):
+        # sequence b's rows start where the previous one ends (room to grow)
+        base = np.concatenate([[0], np.cumsum([n + steps for n in start])])[:-1]
+        ent = [0]
+        for n in lens:
+            for _ in range(g):
+                ent.append(ent[-1] + n)
+        d_start.copy_(torch.tensor([int(base[e // g]) for e in range(entries)], dtype=torch.int32))
+        d_ind.copy_(torch.tensor(ent, dtype=torch.int32))
+        torch.cuda.synchronize()
+        return base
+
+    lens = list(start)
+    upload(lens)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        dev.plan(d_ind, stream=s)
+        dev.decode_starts("mxfp4", q, packed, scales, d_start, d_ind, out, sm_scale=SM, stream=s)
+        s.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            dev.plan(d_ind, stream=s)
+            dev.decode_starts("mxfp4", q, packed, scales, d_start, d_ind, out, sm_scale=SM, stream=s)
+    torch.cuda.synchronize()
+    for step in range(steps):
+        lens = [n + 1 for n in lens]
+        base = upload(lens)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        # the same state through a host plan over a contiguous copy of the rows
+        rows = np.concatenate([np.arange(base[b], base[b] + n) for b, n in enumerate(lens)])
+        idx = torch.from_numpy(rows).cuda()
+        ind = np.concatenate([[0], np.cumsum(lens)]).tolist()
+        host = binding.MlaDecodeGroups(ind, g, device="cuda", num_cus=6)
+        want = host.mxfp4(q, packed[idx].contiguous(), scales[idx].contiguous(), sm_scale=SM)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"step {step}"
