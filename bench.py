@@ -247,7 +247,7 @@ def main(argv=None):
         q = (torch.randn(groups.batch, 16, 576, generator=gq) * w.q_std).to(torch.bfloat16).to(dev)
         out = torch.empty(groups.batch, 16, 512, dtype=torch.bfloat16, device=dev)
         dec = groups.plan
-        words, _ = binding.plan_host(dec.indptr_host, binding.num_cus())
+        words, _ = binding.plan_host(dec.indptr_host, groups.num_cus)
 
         def call():
             binding.decode_starts(fmt, q, packed, scales, groups.kv_start, dec.kv_indptr, out, w.sm_scale,

@@ -117,6 +117,9 @@ def num_cus() -> int:
     return n.value
 
 
+_device_num_cus = num_cus   # for callers whose own argument is named num_cus
+
+
 def workspace_bytes(batch: int, total_kv: int, num_cus: int = 0) -> int:
     out = ctypes.c_size_t(0)
     _check(lib().mla_workspace_bytes(batch, total_kv, num_cus, ctypes.byref(out)),
@@ -483,6 +486,14 @@ class MlaDecodeGroups:
                 entry.append(entry[-1] + n)
         if entry[-1] >= 2 ** 31:
             raise ValueError("more than 2^31 - 1 tokens over all entries")
+        if num_cus == 0:
+            # up to one slot per entry (at most 4 per CU): the entries of a
+            # sequence then hold consecutive slots that run at the same time
+            # on one XCD and share its L2, instead of following each other
+            # on one CU
+            cus = _device_num_cus()
+            num_cus = cus * max(1, min(4, -(-(len(entry) - 1) // cus)))
+        self.num_cus = num_cus   # the slot count the plan spreads the entries over
         self.plan = MlaDecode(entry, device=device, num_cus=num_cus)
         self.batch = self.plan.batch
         self.device = self.plan.device
