@@ -460,6 +460,23 @@ class MlaDecodePageTable:
         return self._run("bf16", q, kv_bf16, None, page_indices, out, sm_scale, stream, check, 2 * QK_DIM)
 
 
+def group_entries(kv_indptr, groups: int):
+    """Plan offsets and start rows of ``groups`` query entries per sequence:
+    entry e = b * groups + g has sequence b's length and starts at its first
+    row. Returns (entry offsets [B * groups + 1], start rows [B * groups])."""
+    ind = [int(v) for v in kv_indptr]
+    if groups < 1:
+        raise ValueError("groups must be >= 1")
+    entry, starts = [0], []
+    for a, b in zip(ind, ind[1:]):
+        for _ in range(groups):
+            entry.append(entry[-1] + (b - a))
+            starts.append(a)
+    if entry[-1] >= 2 ** 31:
+        raise ValueError("more than 2^31 - 1 tokens over all entries")
+    return entry, starts
+
+
 class MlaDecodeGroups:
     """A planned decode where every sequence of a contiguous cache serves
     ``groups`` consecutive 16-head query entries: entry e = b * groups + g
@@ -475,17 +492,9 @@ class MlaDecodeGroups:
     def __init__(self, kv_indptr, groups: int, device="cuda", num_cus: int = 0):
         import torch
         ind = [int(v) for v in kv_indptr]
-        if groups < 1:
-            raise ValueError("groups must be >= 1")
         self.groups = int(groups)
         self.indptr_host = ind
-        lens = [b - a for a, b in zip(ind, ind[1:])]
-        entry = [0]
-        for n in lens:
-            for _ in range(self.groups):
-                entry.append(entry[-1] + n)
-        if entry[-1] >= 2 ** 31:
-            raise ValueError("more than 2^31 - 1 tokens over all entries")
+        entry, starts = group_entries(ind, self.groups)
         if num_cus == 0:
             # up to one slot per entry (at most 4 per CU): the entries of a
             # sequence then hold consecutive slots that run at the same time
@@ -498,7 +507,6 @@ class MlaDecodeGroups:
         self.batch = self.plan.batch
         self.device = self.plan.device
         self.kv_indptr = self.plan.kv_indptr
-        starts = [ind[e // self.groups] for e in range(self.batch)]
         self.kv_start = torch.tensor(starts if starts else [0], dtype=torch.int32, device=self.device)
 
     def _run(self, fmt, q, pool, kv_scale, out, sm_scale, stream):

@@ -33,6 +33,8 @@ def test_algorithmic_bytes():
     assert bench.algorithmic_bytes(words, 256 * 8192) == 650641408
     assert bench.algorithmic_bytes(words, 256 * 8192, "fp8") == 1216872448
     assert bench.algorithmic_bytes(words, 256 * 8192, gather=True) == 650641408 + 4 * 256 * 8192
+    # through a page table: one 4-byte entry per page, not per token
+    assert bench.algorithmic_bytes(words, 256 * 8192, pages=256 * 8192 // 16) == 650641408 + 4 * 256 * 8192 // 16
     words[9] = 3            # each partial written once and read once
     assert bench.algorithmic_bytes(words, 0) - bench.algorithmic_bytes([0] * 16, 0) == \
         256 * bench.QO_BYTES_PER_SEQ + 2 * 3 * 16 * 513 * 4
@@ -109,3 +111,17 @@ def test_page_table_offsets_and_guards():
         binding.check_page_table(torch.tensor([0], dtype=torch.int32), [0, 2], [1], 4, pool_rows=64)
     with pytest.raises(ValueError):   # wrong dtype
         binding.check_page_table(torch.tensor([0], dtype=torch.int64), [0, 1], [1], 4, pool_rows=64)
+
+
+def test_grouped_entries_layout():
+    """128 heads as 8 groups: entry e = b * 8 + g has sequence b's length and
+    starts at its first row; the host planner takes the entries as its
+    sequences."""
+    entry, starts = binding.group_entries([3, 8, 8, 15], 8)
+    assert entry == [0] + [5 * k for k in range(1, 9)] + [40] * 8 + [40 + 7 * k for k in range(1, 9)]
+    assert starts == [3] * 8 + [8] * 8 + [8] * 8
+    assert binding.group_entries([0, 4], 1) == ([0, 4], [0])
+    with pytest.raises(ValueError):
+        binding.group_entries([0, 4], 0)
+    words, _ = binding.plan_host(entry, 256)
+    assert words[2] == 24 and words[4] == 8 * (5 + 7)   # entries and their tokens
