@@ -330,3 +330,52 @@ def test_growing_page_table_replayed_in_a_graph():
     exp = ref.mla_decode_ref_page_table(_qbits(q), pool_p.cpu().numpy(), pool_s.cpu().numpy(),
                                         d_pages[: int(pi[-1])].cpu().numpy(), pi, last, ps, SM)
     _check(out.float().cpu().numpy(), exp, "growing page table, last step")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_rows_at_the_top_of_the_largest_pool(fmt):
+    """Row lists and page tables reading the last rows of the largest pool
+    the 32-bit offsets allow (pool bytes just under 2^32) give the same bits
+    as the contiguous decode of those rows."""
+    row_bytes = 288 if fmt == "mxfp4" else 576
+    ps = 16
+    rows_max = (2 ** 32 - 1) // row_bytes // ps * ps          # whole pages, pool below 2^32 bytes
+    assert rows_max * row_bytes < 2 ** 32
+    lens = [70, 33]
+    _say(f"case largest pool {fmt}: {rows_max} rows")
+    w = synth.Workload("top", len(lens), None, None, 1.0, False, 9)
+    if fmt == "mxfp4":
+        q, packed, scales, indptr, _ = synth.make_inputs(w, lengths=lens)
+        cache = (packed.cuda(), scales.cuda())
+        scale = None
+    else:
+        q, c, scale, indptr, _ = synth.make_dense_inputs(w, fmt, lengths=lens)
+        cache = (c.cuda(),)
+        scale = scale.cuda()
+    q = q.cuda()
+    total = int(indptr[-1])
+    # sequence b's pages are the last pages of the pool, in reverse order
+    npages = [(n + ps - 1) // ps for n in lens]
+    pi = np.concatenate([[0], np.cumsum(npages)])
+    pages = np.arange(rows_max // ps - 1, rows_max // ps - 1 - int(pi[-1]), -1).astype(np.int32)
+    last = [n - (p - 1) * ps for n, p in zip(lens, npages)]
+    rows = np.concatenate(pref.page_table_rows(pages, pi, last, ps)).astype(np.int64)
+    assert rows.min() >= 0 and rows.max() <= rows_max - 1 and rows.max() >= rows_max - ps
+    pool = [torch.empty((rows_max,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda") for x in cache]
+    ridx = torch.from_numpy(rows).cuda()
+    for p, x in zip(pool, cache):
+        p[ridx] = x
+    plain = binding.MlaDecode(indptr.tolist(), device="cuda")
+    if fmt == "mxfp4":
+        want = plain(q, cache[0], cache[1], sm_scale=SM).clone()
+        by_rows = plain.mxfp4_paged(q, pool[0], pool[1], ridx.to(torch.int32), sm_scale=SM).clone()
+    else:
+        want = plain.fp8(q, cache[0], scale, sm_scale=SM).clone()
+        by_rows = plain.fp8_paged(q, pool[0], scale, ridx.to(torch.int32), sm_scale=SM).clone()
+    dec = binding.MlaDecodePageTable(pi.tolist(), last, ps, device="cuda")
+    by_pages = _run(dec, fmt, q, tuple(pool), scale, torch.from_numpy(pages).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(by_rows, want), "row list at the top of the pool"
+    assert torch.equal(by_pages, want), "page table at the top of the pool"
+    del pool
+    torch.cuda.empty_cache()
