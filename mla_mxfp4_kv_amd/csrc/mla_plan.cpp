@@ -70,6 +70,9 @@ int build_plan(const int32_t* ind, int32_t batch, int32_t num_cus, PlanResult* o
   int64_t chunk = 0, num_slots = 0;
   if (total > 0) {
     chunk = std::max<int64_t>(MLA_PLAN_MIN_CHUNK, round_up(ceil_div(total, g), MLA_PLAN_CHUNK_ALIGN));
+    // the chunk is an int32 plan word: one past INT32_MAX covers the whole
+    // stream anyway, and is stored as its length (the same single slot)
+    if (chunk > INT32_MAX) chunk = total;
     num_slots = ceil_div(total, chunk);
   }
 

@@ -87,6 +87,7 @@ mla_plan_kernel(const int32_t* __restrict__ ind, int32_t batch, int32_t num_cus,
     const int64_t per = (total + g - 1) / g;
     const int64_t aligned = (per + MLA_PLAN_CHUNK_ALIGN - 1) / MLA_PLAN_CHUNK_ALIGN * MLA_PLAN_CHUNK_ALIGN;
     chunk = aligned > MLA_PLAN_MIN_CHUNK ? aligned : MLA_PLAN_MIN_CHUNK;
+    if (chunk > INT32_MAX) chunk = total;   // an int32 plan word; the same single slot
     num_slots = (total + chunk - 1) / chunk;
   }
   int32_t* slot_indptr = w + MLA_PLAN_HEADER_WORDS;

@@ -16,7 +16,9 @@ every workgroup streams the same number of KV bytes whatever the length mix.
 The rule (constants in ``PlanConsts``):
 
 * ``T = kv_indptr[B] - kv_indptr[0]``, ``G = num_cus * WG_PER_CU``.
-* ``chunk = max(MIN_CHUNK, round_up(ceil(T / G), CHUNK_ALIGN))``;
+* ``chunk = max(MIN_CHUNK, round_up(ceil(T / G), CHUNK_ALIGN))``, or T when
+  that exceeds 2^31 - 1 (the chunk is an int32 plan word; either value
+  gives the same single slot);
   ``num_slots = ceil(T / chunk)`` (0 when T is 0).
 * Slot s owns tokens ``[base + s*chunk, min(base + (s+1)*chunk, base + T))``.
 * The slot's range is cut at sequence boundaries, in ascending token order,
@@ -98,6 +100,8 @@ def build_plan(kv_indptr, batch: int, num_cus: int) -> PlanRef:
         chunk, num_slots = 0, 0
     else:
         chunk = max(c.MIN_CHUNK, _round_up(_cdiv(total, g), c.CHUNK_ALIGN))
+        if chunk > 2 ** 31 - 1:   # the chunk word is int32; the one slot it defines covers T
+            chunk = total
         num_slots = _cdiv(total, chunk)
 
     plan = PlanRef(batch=batch, base=base, total=total, num_cus=num_cus, chunk=chunk)

@@ -90,3 +90,11 @@ def test_workspace_bytes_rejects_bad_sizes():
         binding.workspace_bytes(-1, 10, 4)
     with pytest.raises(binding.MlaError):
         binding.workspace_bytes(1, -10, 4)
+
+
+def test_host_plan_at_the_int32_token_limit():
+    """Offsets up to 2^31 - 1 (the largest int32 kv_indptr): the plan words
+    still equal the planner oracle's, split over every CU count tried."""
+    for ind in ([0, 2 ** 30, 2 ** 31 - 1], [5, 2 ** 31 - 1], [0, 1, 2 ** 31 - 2, 2 ** 31 - 1]):
+        for cus in (1, 256):
+            assert binding.plan_host(ind, cus) == plan_words_ref(ind, len(ind) - 1, cus)

@@ -62,6 +62,7 @@ PLAN_CASES = [
     ([40, 0, 300, 129], 77, 3),
     ([256] * 10, 0, 10),
     ([255, 257, 1, 511, 513], 5, 7),
+    ([2 ** 30, 2 ** 31 - 1 - 2 ** 30], 0, 1),     # the int32 token limit on one CU
 ]
 
 
@@ -72,7 +73,7 @@ def test_device_plan_words_match_oracle(lens, base, num_cus):
     batch = len(lens)
     total = ind[-1] - ind[0]
     want = pref.build_plan(ind, batch, num_cus)
-    dp = binding.MlaDecodeDevicePlan(batch, total + 1000, num_cus=num_cus)
+    dp = binding.MlaDecodeDevicePlan(batch, min(total + 1000, 2 ** 31 - 1), num_cus=num_cus)
     dp.plan(torch.tensor(ind, dtype=torch.int32, device="cuda"))
     got = _device_words(dp)
     assert got["magic"] == pref.PlanConsts.MAGIC
