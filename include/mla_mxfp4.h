@@ -87,7 +87,10 @@ int mla_device_num_cus(int32_t* num_cus);
  * `total_kv` tokens needs on a device with `num_cus` compute units
  * (num_cus <= 0: query the current device). The workspace holds the plan
  * words followed by the split-K partials (float32 LSE [P,16] and normalised
- * float32 outputs [P,16,512]). */
+ * float32 outputs [P,16,512]). MLA_ERR_INVALID for batch < 0, total_kv
+ * outside [0, 2^31), or sizes whose worst-case plan would start its
+ * partial outputs past the int32 byte offsets a plan stores (tens of
+ * millions of sequences). */
 int mla_workspace_bytes(int32_t batch, int64_t total_kv, int32_t num_cus, size_t* bytes);
 
 /* Build the work list for a host copy of kv_indptr ([batch+1]) and copy it

@@ -107,6 +107,10 @@ int mla_workspace_bytes(int32_t batch, int64_t total_kv, int32_t num_cus, size_t
     const int st = mla_device_num_cus(&num_cus);
     if (st != MLA_OK) return st;
   }
+  // the plans a bound covers address their partials with int32 offsets
+  // (mla_plan_device refuses the same layout)
+  if (mla::device_layout(batch, total_kv, num_cus).off_out > INT32_MAX)
+    return fail(MLA_ERR_INVALID, "these sizes exceed the int32 offsets of a plan");
   *bytes = mla::workspace_bound(batch, total_kv, num_cus);
   return MLA_OK;
 }

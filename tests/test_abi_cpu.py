@@ -90,6 +90,13 @@ def test_workspace_bytes_rejects_bad_sizes():
         binding.workspace_bytes(-1, 10, 4)
     with pytest.raises(binding.MlaError):
         binding.workspace_bytes(1, -10, 4)
+    # a layout whose partial outputs would start past the int32 byte offsets
+    # of a plan (the GPU-side planner refuses the same layout); only the
+    # start is an int32 word, so a large partial area itself is fine
+    with pytest.raises(binding.MlaError):
+        binding.workspace_bytes(2 ** 31 - 1, 2 ** 31 - 1, 256)
+    assert binding.workspace_bytes(10 ** 6, 2 ** 31 - 1, 256) > 0
+    assert binding.workspace_bytes(1, 2 ** 31 - 1, 2 ** 20) > 2 ** 31
 
 
 def test_host_plan_at_the_int32_token_limit():
