@@ -105,3 +105,25 @@ def test_host_plan_at_the_int32_token_limit():
     for ind in ([0, 2 ** 30, 2 ** 31 - 1], [5, 2 ** 31 - 1], [0, 1, 2 ** 31 - 2, 2 ** 31 - 1]):
         for cus in (1, 256):
             assert binding.plan_host(ind, cus) == plan_words_ref(ind, len(ind) - 1, cus)
+
+
+def test_host_plan_matches_oracle_property():
+    """Property test: any non-decreasing int32 offsets (bases and lengths up
+    to the int32 limit, empty sequences, lengths near chunk edges) plan to
+    the oracle's words on any CU count."""
+    from hypothesis import given, settings, HealthCheck, strategies as st
+
+    lens_st = st.lists(st.one_of(st.integers(0, 300), st.integers(0, 2 ** 20),
+                                 st.sampled_from([127, 128, 129, 255, 256, 257, 8192])), min_size=0, max_size=40)
+
+    @settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+    @given(lens=lens_st, base=st.one_of(st.just(0), st.integers(0, 2 ** 31 - 1)), cus=st.integers(1, 300))
+    def check(lens, base, cus):
+        ind = [base]
+        for n in lens:
+            ind.append(ind[-1] + n)
+        if ind[-1] > 2 ** 31 - 1:
+            return
+        assert binding.plan_host(ind, cus) == plan_words_ref(ind, len(lens), cus)
+
+    check()
