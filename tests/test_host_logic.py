@@ -125,3 +125,20 @@ def test_grouped_entries_layout():
         binding.group_entries([0, 4], 0)
     words, _ = binding.plan_host(entry, 256)
     assert words[2] == 24 and words[4] == 8 * (5 + 7)   # entries and their tokens
+
+
+def test_page_table_offsets_match_the_oracle():
+    """The binding's token offsets of random page tables equal the oracle's,
+    and the oracle's page-by-page rows have those lengths."""
+    import numpy as np
+    from oracle import paging_ref as pref
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        ps = int(rng.integers(1, 70))
+        npages = rng.integers(0, 6, 5)
+        pi = np.concatenate([[0], np.cumsum(npages)]).tolist()
+        last = [int(rng.integers(1, ps + 1)) if n else 0 for n in npages]
+        tok = binding.page_table_kv_indptr(pi, last, ps)
+        assert tok == pref.page_table_token_indptr(pi, last, ps).tolist()
+        rows = pref.page_table_rows(np.arange(pi[-1]), pi, last, ps)
+        assert [len(r) for r in rows] == [b - a for a, b in zip(tok, tok[1:])]
