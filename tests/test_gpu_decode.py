@@ -392,3 +392,40 @@ def test_workload_b128_ragged():
         order = np.argsort(lens)
         return sorted({int(order[0]), int(order[-1]), 5, 64, 127})
     _sampled_workload_check("b128_ragged", pick)
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        b = int(rng.integers(1, 7))
+        lens = [int(rng.choice([0, 1, int(rng.integers(1, 300)), int(rng.integers(1, 3000)),
+                                int(rng.choice([31, 32, 33, 127, 128, 129, 255, 256, 257]))])) for _ in range(b)]
+        yield lens, int(rng.choice([0, 1, 3, 7, 16]))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8", "bf16"])
+def test_random_shapes_match_oracle(fmt):
+    """Seeded random batches (empty, one-token, tile-edge and long
+    sequences) on several CU counts, every element against the oracle."""
+    from oracle import dense_ref as dref
+    for k, (lens, cus) in enumerate(_random_shapes(8, {"mxfp4": 1, "fp8": 2, "bf16": 3}[fmt])):
+        _say(f"case random {fmt} #{k} lens={lens} num_cus={cus}")
+        w = synth.Workload("r", len(lens), None, None, 1.0, False, 100 + k)
+        dec = None
+        if fmt == "mxfp4":
+            q, packed, scales, indptr, _ = synth.make_inputs(w, lengths=lens)
+            dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=cus)
+            out = dec(q.cuda(), packed.cuda(), scales.cuda(), sm_scale=SM)
+            want = ref.mla_decode_ref(_qbits(q), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+        else:
+            q, cache, scale, indptr, _ = synth.make_dense_inputs(w, fmt, lengths=lens)
+            dec = binding.MlaDecode(indptr.tolist(), device="cuda", num_cus=cus)
+            if fmt == "fp8":
+                out = dec.fp8(q.cuda(), cache.cuda(), scale.cuda(), sm_scale=SM)
+                want = dref.mla_decode_ref_fp8(_qbits(q), cache.numpy(), float(scale[0]), indptr.numpy(), SM)
+            else:
+                out = dec.bf16(q.cuda(), cache.cuda(), sm_scale=SM)
+                bits = cache.view(torch.int16).numpy().view(np.uint16)
+                want = dref.mla_decode_ref_bf16(_qbits(q), bits, indptr.numpy(), SM)
+        torch.cuda.synchronize()
+        _check(out.float().cpu().numpy(), want, f"random {fmt} #{k} {lens} cus={cus}")
