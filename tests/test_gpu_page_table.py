@@ -379,3 +379,23 @@ def test_rows_at_the_top_of_the_largest_pool(fmt):
     assert torch.equal(by_pages, want), "page table at the top of the pool"
     del pool
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8", "bf16"])
+def test_random_page_tables_match_oracle(fmt):
+    """Seeded random page sizes (1..80), lengths and CU counts, against the
+    page-table oracle."""
+    rng = np.random.default_rng({"mxfp4": 11, "fp8": 12, "bf16": 13}[fmt])
+    for k in range(6):
+        b = int(rng.integers(1, 6))
+        lens = [int(rng.choice([0, 1, int(rng.integers(1, 200)), int(rng.integers(1, 2500))])) for _ in range(b)]
+        ps = int(rng.choice([1, int(rng.integers(2, 17)), 16, 32, int(rng.integers(17, 81))]))
+        cus = int(rng.choice([0, 1, 3, 9]))
+        _say(f"case random page table {fmt} #{k} lens={lens} page_size={ps} num_cus={cus}")
+        q, pool, scale, indptr, pi, last, pages = _case(fmt, lens, ps, seed=1000 + k)
+        dec = binding.MlaDecodePageTable(pi.tolist(), last, ps, device="cuda", num_cus=cus)
+        out = _run(dec, fmt, q.cuda(), tuple(p.cuda() for p in pool), scale.cuda() if scale is not None else None,
+                   torch.from_numpy(pages).cuda())
+        torch.cuda.synchronize()
+        _check(out.float().cpu().numpy(), _oracle(fmt, q, pool, scale, pi, last, pages, ps),
+               f"random page table {fmt} #{k}")
