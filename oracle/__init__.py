@@ -22,6 +22,8 @@ Modules:
 
 * :mod:`oracle.mxfp4_ref` -- exact MXFP4 dequantisation and fp64 attention,
   also over per-token row lists (``mla_decode_ref_gather``).
+* :mod:`oracle.mxfp4_24_ref` -- the layout with 24 E8M0 bytes per token
+  (24-element blocks) from page "kernelbot-amd-mixed-mla-717900".
 * :mod:`oracle.dense_ref` -- exact fp8 (e4m3 + per-tensor scale) and bf16
   cache decoding and the same fp64 attention, for the sibling decodes.
 * :mod:`oracle.paging_ref` -- page tables (page number, page size, valid rows
@@ -65,6 +67,13 @@ from .dense_ref import (  # noqa: F401
     mla_decode_ref_bf16_page_table,
     mla_decode_ref_fp8_groups,
     mla_decode_ref_bf16_groups,
+)
+from .mxfp4_24_ref import (  # noqa: F401
+    SCALE_BLOCK_24,
+    SCALES_PER_TOKEN_24,
+    dequant_mxfp4_24,
+    mla_decode_ref_24,
+    mla_decode_ref_24_seq,
 )
 from .paging_ref import page_table_rows, page_table_token_indptr  # noqa: F401
 from .planner_ref import plan_words_ref, PlanRef, decode_plan_words  # noqa: F401
