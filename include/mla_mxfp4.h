@@ -71,7 +71,7 @@ extern "C" {
 #define MLA_ERR_WORKSPACE -2    /* workspace smaller than the plan needs */
 #define MLA_ERR_HIP -3          /* a HIP runtime call or kernel launch failed */
 #define MLA_ERR_DEVICE -4       /* the current device is not gfx950 */
-#define MLA_ERR_NOT_PLANNED -5  /* workspace was never passed to mla_plan */
+#define MLA_ERR_NOT_PLANNED -5  /* workspace was never passed to mla_plan, or was released */
 
 /* Human-readable name of a status code (static string). */
 const char* mla_status_string(int status);
@@ -143,6 +143,19 @@ int mla_plan_cus(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
 int mla_plan_device(const int32_t* kv_indptr_dev, int32_t batch, int64_t max_total_kv,
                     int32_t num_cus, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forget the plan registered for `workspace` (a host-side record; the
+ * device memory is not touched). Call it before the workspace memory is
+ * freed or reused: a decode on a released workspace returns
+ * MLA_ERR_NOT_PLANNED until it is planned again. The registry is keyed by
+ * address, so a workspace freed without release and reallocated at the
+ * same address would otherwise still find the old record; the decode
+ * kernels then follow the words in the workspace only if its header holds
+ * the plan magic and version (anything else leaves `out` untouched), but
+ * an old plan left intact in the memory cannot be told from a fresh one.
+ * Returns MLA_OK, or MLA_ERR_NOT_PLANNED if no plan was registered.
+ * Thread-safe; needs no GPU. */
+int mla_plan_release(void* workspace);
+
 /* Host-only planner: write the plan words for `num_cus` compute units into
  * `words` (host, `capacity_words` int32 entries). On success *num_words is
  * the word count and *workspace_bytes the workspace size the plan needs.
@@ -157,13 +170,19 @@ int mla_plan_host(const int32_t* kv_indptr_host, int32_t batch, int32_t num_cus,
  * split or empty, the LSE-weighted reduce kernel on `stream`; never
  * synchronises. kv_indptr is the device copy of the offsets the plan was
  * built from; the kernels use it to bound every item to its sequence.
- * sm_scale is the softmax scale (1/sqrt(576) for this model); it must be
- * finite and non-negative.
+ * sm_scale is the softmax scale (1/sqrt(576) for this model); any finite
+ * value (zero gives the plain mean of V, a negative scale favours the
+ * lowest scores, as the definition does).
  *
- * Errors (nothing is enqueued): MLA_ERR_NOT_PLANNED, MLA_ERR_INVALID (null
- * or misaligned pointer, non-finite or negative sm_scale), MLA_ERR_DEVICE,
- * MLA_ERR_HIP (launch failure). Faults inside the kernels surface as HIP
- * errors on the stream. */
+ * The kernels only follow plan words whose header holds MLA_PLAN_MAGIC and
+ * MLA_PLAN_VERSION; a workspace whose header does not (cleared or
+ * overwritten after planning, or an empty device plan) leaves `out`
+ * untouched.
+ *
+ * Errors (nothing is enqueued): MLA_ERR_NOT_PLANNED (checked first, without
+ * any HIP call), MLA_ERR_INVALID (null or misaligned pointer, non-finite
+ * sm_scale), MLA_ERR_DEVICE, MLA_ERR_HIP (launch failure). Faults inside
+ * the kernels surface as HIP errors on the stream. */
 int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                      const int32_t* kv_indptr, void* out, float sm_scale,
                      void* workspace, void* stream);

@@ -25,7 +25,7 @@ SCALES_PER_TOKEN = 18
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
     "mla_status_string", "mla_last_error", "mla_device_num_cus", "mla_workspace_bytes",
-    "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4",
+    "mla_plan", "mla_plan_cus", "mla_plan_device", "mla_plan_release", "mla_plan_host", "mla_decode_mxfp4",
     "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
     "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
     "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts", "mla_decode_bf16_starts",
@@ -63,6 +63,7 @@ def lib():
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.mla_plan_host.argtypes = [c_i32p, ctypes.c_int32, ctypes.c_int32, c_i32p, ctypes.c_size_t,
                                 c_sizep, c_sizep]
+    L.mla_plan_release.argtypes = [ctypes.c_void_p]
     L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_mxfp4_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -86,7 +87,7 @@ def lib():
     L.mla_decode_fp8_starts.argtypes = st
     L.mla_decode_bf16_starts.argtypes = st[:1] + st[2:]
     for name in ("mla_device_num_cus", "mla_workspace_bytes", "mla_plan", "mla_plan_cus",
-                 "mla_plan_device", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
+                 "mla_plan_device", "mla_plan_release", "mla_plan_host", "mla_decode_mxfp4", "mla_decode_fp8",
                  "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
                  "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
                  "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts",
@@ -164,6 +165,20 @@ def plan_device(kv_indptr_dev, batch: int, max_total_kv: int, workspace, num_cus
                                  num_cus, ctypes.c_void_p(workspace.data_ptr()),
                                  workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
            "mla_plan_device")
+
+
+def plan_release(workspace_ptr: int) -> int:
+    """Forget the plan registered for a workspace address (host record only);
+    returns the status (MLA_OK, or -5 when nothing was registered)."""
+    return lib().mla_plan_release(ctypes.c_void_p(workspace_ptr))
+
+
+def _release_on_free(workspace):
+    """Release the workspace's plan record when the tensor is collected, so a
+    later tensor at the same address is refused until it is planned."""
+    import weakref
+    fin = weakref.finalize(workspace, plan_release, workspace.data_ptr())
+    fin.atexit = False
 
 
 def decode(q, kv_packed, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
@@ -339,6 +354,7 @@ class MlaDecode:
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         assert self.workspace.data_ptr() % 256 == 0
         plan(ind, self.workspace, num_cus=num_cus)
+        _release_on_free(self.workspace)
 
     def __call__(self, q, kv_packed, kv_scale, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
         import torch
@@ -552,6 +568,7 @@ class MlaDecodeDevicePlan:
         nbytes = workspace_bytes(batch, max_total_kv, num_cus)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         assert self.workspace.data_ptr() % 256 == 0
+        _release_on_free(self.workspace)
 
     def plan(self, kv_indptr, stream=None):
         import torch

@@ -208,6 +208,13 @@ int mla_plan(const int32_t* kv_indptr_host, int32_t batch, void* workspace, size
   return mla_plan_cus(kv_indptr_host, batch, 0, workspace, workspace_bytes, stream);
 }
 
+int mla_plan_release(void* workspace) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_plans.erase((uintptr_t)workspace) == 0)
+    return fail(MLA_ERR_NOT_PLANNED, "workspace has no plan to release");
+  return MLA_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -221,21 +228,22 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
                   void* workspace, void* stream, bool gather = false,
                   const int32_t* page_indptr = nullptr, int32_t page_size = 1,
                   const int32_t* kv_start = nullptr) {
-  int dev;
-  DeviceInfo info;
-  int st = current_device(&dev, &info);
-  if (st != MLA_OK) return st;
+  // The registry is consulted before any HIP call: a workspace that was
+  // never planned, or was released, is refused without touching the device.
   PlanEntry pe;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     auto it = g_plans.find((uintptr_t)workspace);
     if (it == g_plans.end())
-      return fail(MLA_ERR_NOT_PLANNED, "workspace was not prepared by mla_plan");
+      return fail(MLA_ERR_NOT_PLANNED, "workspace was not prepared by mla_plan (or was released)");
     pe = it->second;
   }
+  int dev;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != MLA_OK) return st;
   if (pe.device != dev) return fail(MLA_ERR_INVALID, "workspace was planned on another device");
-  if (!std::isfinite(sm_scale) || sm_scale < 0.0f)
-    return fail(MLA_ERR_INVALID, "sm_scale must be finite and non-negative");
+  if (!std::isfinite(sm_scale)) return fail(MLA_ERR_INVALID, "sm_scale must be finite");
   const bool any_work = pe.num_slots > 0 || pe.num_reduce > 0;
   if (any_work) {
     if (out == nullptr || !aligned(out, 16)) return fail(MLA_ERR_INVALID, "out must be non-null and 16-byte aligned");

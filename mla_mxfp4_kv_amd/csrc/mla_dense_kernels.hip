@@ -498,6 +498,9 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
+  // Only words written by a planner are followed: a workspace whose header
+  // is not a plan of this version leaves the output untouched.
+  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
   // V scale and base-2 logit scale: the per-tensor fp8 scale multiplies both
   float vs = 1.0f;
   if constexpr (kFp8) vs = kv_scale[0];
@@ -532,8 +535,12 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
       // contiguous rows from kv_start[b] on, when given (shared by sequences)
       const uint8_t* kv_b = kv;
       if (!kGather && kv_start != nullptr) kv_b += ((ptrdiff_t)kv_start[b] - seq_lo) * C::kRow;
-      const int t_first = kb + C::kTile * wave;
-      const int ntiles = t_first < ke ? (ke - t_first + C::kStride - 1) / C::kStride : 0;
+      // counts from differences, so that offsets near 2^31 - 1 cannot wrap;
+      // a tile start is only formed for tiles inside the item (below ke)
+      const int len = ke - kb;
+      const int rel_first = C::kTile * wave;
+      const int ntiles = rel_first < len ? (len - rel_first - 1) / C::kStride + 1 : 0;
+      const int t_first = ntiles > 0 ? kb + rel_first : kb;
 
       const uint16_t* qh = q + ((size_t)b * kHeads + col) * kQkDim;
       QFp8 q8;
@@ -574,12 +581,13 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
         }
 #pragma unroll
         for (int j = 0; j < 4 * C::kSub; ++j) x[j] *= sc2;
-        if (t0 + C::kTile > ke) {   // tail tile: tokens past the item get p = 0
+        const int nvalid = ke - t0;   // a difference: no wrap near 2^31 - 1
+        if (nvalid < C::kTile) {   // tail tile: tokens past the item get p = 0
 #pragma unroll
           for (int s = 0; s < C::kSub; ++s)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (t0 + 16 * s + 4 * grp + r >= ke) x[4 * s + r] = kNegInf;
+              if (16 * s + 4 * grp + r >= nvalid) x[4 * s + r] = kNegInf;
         }
         float mx = x[0];
 #pragma unroll

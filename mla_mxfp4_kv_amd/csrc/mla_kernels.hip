@@ -436,7 +436,9 @@ __device__ __forceinline__ void split16(const float* x, int sh, int* hi, int* lo
   }
 }
 
-__device__ __forceinline__ QOperands load_q(const uint16_t* qh, int grp) {
+// `sign` (0 or 0x80008000) is xored into every pair of bf16 values: a
+// negative softmax scale is applied as |scale| on -q, which is exact.
+__device__ __forceinline__ QOperands load_q(const uint16_t* qh, int grp, uint32_t sign) {
   QOperands f;
   f.sc_hi = 0u;
   f.sc_lo = 0u;
@@ -444,7 +446,7 @@ __device__ __forceinline__ QOperands load_q(const uint16_t* qh, int grp) {
   for (int m = 0; m < 4; ++m) {
     const u32x4_t* p0 = (const u32x4_t*)(qh + 128 * m + 16 * grp);
     const u32x4_t* p1 = (const u32x4_t*)(qh + 128 * m + 64 + 16 * grp);
-    const u32x4_t w[4] = {p0[0], p0[1], p1[0], p1[1]};
+    const u32x4_t w[4] = {p0[0] ^ sign, p0[1] ^ sign, p1[0] ^ sign, p1[1] ^ sign};
     float x[32];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -479,7 +481,8 @@ __device__ __forceinline__ QOperands load_q(const uint16_t* qh, int grp) {
     f.sc_lo |= (uint32_t)max(sup - 4, 0) << (8 * m);
   }
 #pragma unroll
-  for (int s = 0; s < 2; ++s) f.rope[s] = *(const bf16x8_t*)(qh + 512 + 16 * grp + 8 * s);
+  for (int s = 0; s < 2; ++s)
+    f.rope[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qh + 512 + 16 * grp + 8 * s) ^ sign);
   return f;
 }
 
@@ -530,15 +533,19 @@ __device__ __forceinline__ f32x4_t qk_subtile(const uint8_t* buf, int delta, int
 // 4*grp + r of the first sub-tile, s1: of the second, for head `col`):
 // returns the tile's hand-off to the P V wave and folds the bf16-rounded
 // P into l.
-__device__ __forceinline__ TileHandoff softmax_tile(f32x4_t s0, f32x4_t s1, int t0, int ke,
+// `csc` >= 0 (a negative scale reaches here as |scale| with q negated).
+// `nvalid` = tokens of the tile inside the item (ke - t0, computed as a
+// difference so that offsets near 2^31 cannot wrap).
+__device__ __forceinline__ TileHandoff softmax_tile(f32x4_t s0, f32x4_t s1, int nvalid,
                                                     SoftmaxState& st, float csc, int lane) {
   const int grp = lane >> 4;
   float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  if (t0 + kTile > ke) {   // tail tile: mask tokens past the item
+  const bool tail = nvalid < kTile;
+  if (tail) {   // tail tile: tokens past the item take no part in the max
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (t0 + 4 * grp + r >= ke) x[r] = kNegInf;
-      if (t0 + 16 + 4 * grp + r >= ke) x[4 + r] = kNegInf;
+      if (4 * grp + r >= nvalid) x[r] = kNegInf;
+      if (16 + 4 * grp + r >= nvalid) x[4 + r] = kNegInf;
     }
   }
   float mx = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), fmaxf(x[6], x[7]));
@@ -558,6 +565,15 @@ __device__ __forceinline__ TileHandoff softmax_tile(f32x4_t s0, f32x4_t s1, int 
   float p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], csc, -base));
+  if (tail) {
+    // p = 0 past the item, set after the exponential: with a zero scale the
+    // masked -inf * 0 would be NaN
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * grp + r >= nvalid) p[r] = 0.f;
+      if (16 + 4 * grp + r >= nvalid) p[4 + r] = 0.f;
+    }
+  }
   const bf16x8_t pa = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                        (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
   // l += sum_t P[h][t] of the same bf16-rounded P that multiplies V
@@ -663,6 +679,14 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
+  // Only words written by a planner are followed: a workspace whose header
+  // is not a plan of this version (never planned, overwritten, or an
+  // empty device plan) leaves the output untouched.
+  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
+  // A negative scale is applied as |scale| on -q (exact), so the running
+  // max below is a max of the scaled scores whatever the scale's sign.
+  const uint32_t qsign = csc < 0.f ? 0x80008000u : 0u;
+  csc = fabsf(csc);
 
   const int num_slots = plan[kPwNumSlots];
   const int32_t* slot_indptr = plan + plan[kPwOffSlot];
@@ -703,10 +727,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         sc_b += shift * kBlocks;
       }
 
+      // counts from differences, so that offsets near 2^31 - 1 cannot wrap;
+      // a tile start is only formed for tiles inside the item (below ke)
       const int len = ke - kb;
-      const int rounds = len > 0 ? (len + kTileStride - 1) / kTileStride : 0;
-      const int t_first = kb + kTile * pair;
-      const int ntiles = t_first < ke ? (ke - t_first + kTileStride - 1) / kTileStride : 0;
+      const int rounds = len > 0 ? (len - 1) / kTileStride + 1 : 0;
+      const int rel_first = kTile * pair;
+      const int ntiles = rel_first < len ? (len - rel_first - 1) / kTileStride + 1 : 0;
+      const int t_first = ntiles > 0 ? kb + rel_first : kb;
 
       // The pair splits a tile's work by role, each wave on its own loop
       // (both pass the same workgroup barriers, one per round):
@@ -722,7 +749,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         SoftmaxState st;
         st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
         st.m = kMInit;
-        const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp);
+        const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp, qsign);
         PageRows pages = {0u, 0u};   // page tables: the entries of the next tile to stage
         __syncthreads();  // LDS of the previous item's merge is free again
         if (ntiles > 0) {
@@ -778,7 +805,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
             const int dq = kGather ? (int)((uintptr_t)sc & 15) : raw_delta(sc_b, tq);
             const f32x4_t s0 = qk_subtile<kGather>(bq, dq, 0, qo, lane);
             const f32x4_t s1 = qk_subtile<kGather>(bq, dq, 1, qo, lane);
-            hand[(i & 1) * (kPairs * 64)] = softmax_tile(s0, s1, tq, ke, st, csc, lane);
+            hand[(i & 1) * (kPairs * 64)] = softmax_tile(s0, s1, ke - tq, st, csc, lane);
             uint8_t* fm = fmt_pair + (i & 1) * (kPairs * kFmtTile);
             format_scales<kGather>(bq, fm, dq, ke - tq, lane);
             format_scales<kGather>(bq, fm, dq, ke - tq, 64 + lane);
@@ -890,6 +917,7 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
   __shared__ float wsum_s[kReduceWaves];
   __shared__ float max_s[kReduceWaves];
   // a plan built on the GPU is launched for its bound on the entry count
+  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
   if ((int)blockIdx.x >= plan[kPwNumReduce]) return;
   const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
   const int b = ent[0];
@@ -969,6 +997,7 @@ static_assert(kVDim == 8 * kNarrowThreads, "narrow reduce: a lane covers 8 dims"
 __global__ void __launch_bounds__(kNarrowThreads)
 mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
                          const float* __restrict__ part_out, uint16_t* __restrict__ out) {
+  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
   if ((int)blockIdx.x >= plan[kPwNumReduce]) return;
   const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
   const int b = ent[0];

@@ -14,8 +14,10 @@ Recipe (one generator, draws in a fixed order: lengths, Q, KV):
   by ``2^u`` with u ~ U[-2, 2] (scales log-uniform in [0.25, 4]), rounded to
   bf16, then MXFP4-encoded by :func:`quantize_mxfp4`.
 
-The rows are generated in fixed-size chunks so that a given (seed, device)
-always yields the same bytes whatever the total size.
+Every draw comes from one CPU ``torch.Generator`` seeded per workload, in
+fixed-size row chunks, so a seed always yields the same bytes whatever the
+total size and whatever ``device`` is: only the bf16 rows are moved to the
+device, where the (exact, integer-valued) MXFP4 encoding runs.
 
 The fp8 and bf16 sibling caches (:func:`make_dense_inputs`) take the same
 draws: the bf16 latent rows as they are, or those rows encoded as OCP E4M3
@@ -115,18 +117,18 @@ def _draw(w: Workload, device, lengths):
     for n in lens:
         indptr.append(indptr[-1] + n)
     total = indptr[-1]
-    g = torch.Generator(device=device).manual_seed(w.seed + 1000)
-    q = (torch.randn(batch, NUM_HEADS, QK_DIM, generator=g, device=device,
-                     dtype=torch.float32) * w.q_std).to(torch.bfloat16)
+    g = torch.Generator().manual_seed(w.seed + 1000)   # CPU: the bytes do not depend on `device`
+    q = (torch.randn(batch, NUM_HEADS, QK_DIM, generator=g, dtype=torch.float32)
+         * w.q_std).to(torch.bfloat16).to(device)
 
     def rows():
         for r0 in range(0, total, _ROW_CHUNK):
             r1 = min(total, r0 + _ROW_CHUNK)
-            x = torch.randn(r1 - r0, QK_DIM, generator=g, device=device, dtype=torch.float32)
+            x = torch.randn(r1 - r0, QK_DIM, generator=g, dtype=torch.float32)
             if w.token_scale:
-                u = torch.rand(r1 - r0, 1, generator=g, device=device, dtype=torch.float32)
+                u = torch.rand(r1 - r0, 1, generator=g, dtype=torch.float32)
                 x = x * torch.exp2(4.0 * u - 2.0)
-            yield r0, r1, x.to(torch.bfloat16)
+            yield r0, r1, x.to(torch.bfloat16).to(device)
 
     return lens, torch.tensor(indptr, dtype=torch.int32), total, q, rows()
 

@@ -127,3 +127,24 @@ def test_host_plan_matches_oracle_property():
         assert binding.plan_host(ind, cus) == plan_words_ref(ind, len(lens), cus)
 
     check()
+
+
+def test_decode_on_an_unplanned_workspace_is_refused_without_a_device():
+    """The plan registry is consulted before any HIP call: a workspace
+    address that was never planned (or was released) gives
+    MLA_ERR_NOT_PLANNED, for every decode entry point, with no GPU."""
+    L = binding.lib()
+    fake = ctypes.c_void_p(0x7F0000100000)
+    p = [ctypes.c_void_p(0x7F0000200000 + 256 * i) for i in range(8)]
+    calls = {
+        "mla_decode_mxfp4": (p[0], p[1], p[2], p[3], p[4], ctypes.c_float(0.1), fake, None),
+        "mla_decode_fp8": (p[0], p[1], p[2], p[3], p[4], ctypes.c_float(0.1), fake, None),
+        "mla_decode_bf16": (p[0], p[1], p[3], p[4], ctypes.c_float(0.1), fake, None),
+        "mla_decode_mxfp4_paged": (p[0], p[1], p[2], p[5], p[3], p[4], ctypes.c_float(0.1), fake, None),
+        "mla_decode_mxfp4_starts": (p[0], p[1], p[2], p[5], p[3], p[4], ctypes.c_float(0.1), fake, None),
+    }
+    for name, args in calls.items():
+        assert getattr(L, name)(*args) == -5, name
+        assert b"not prepared" in L.mla_last_error()
+    assert L.mla_plan_release(fake) == -5
+    assert b"no plan" in L.mla_last_error()

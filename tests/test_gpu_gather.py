@@ -149,7 +149,7 @@ def test_gather_errors():
 
 def test_gather_workload_b256_page_shuffled():
     """The headline workload with its rows scattered over the pool in 16-row
-    pages (a paged cache), checked on sampled sequences."""
+    pages (a paged cache), every sequence against the oracle."""
     w = synth.WORKLOADS["b256_kv8192"]
     _say("case gather b256_kv8192: generating")
     q, packed, scales, indptr, lens = synth.make_inputs(w, device="cuda")
@@ -166,13 +166,14 @@ def test_gather_workload_b256_page_shuffled():
     out = dec.mxfp4_paged(q, pool_p, pool_s, idx, sm_scale=w.sm_scale)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
     qb = _qbits(q)
     ind = indptr.numpy()
-    for b in (0, 131, 255):
+    pk, sc = packed.cpu().numpy(), scales.cpu().numpy()
+    for b in range(len(lens)):
         lo, hi = int(ind[b]), int(ind[b + 1])
-        want = ref.mla_decode_ref_seq(qb[b], packed[lo:hi].cpu().numpy(), scales[lo:hi].cpu().numpy(), w.sm_scale)
+        want = ref.mla_decode_ref_seq(qb[b], pk[lo:hi], sc[lo:hi], w.sm_scale)
         _check(got[b], want, f"b256 gather b={b}")
-    assert np.all(np.isfinite(got))
 
 
 def _dense_case(fmt, lens, seed, extra=2.0):
