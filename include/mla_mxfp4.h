@@ -187,6 +187,28 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                      const int32_t* kv_indptr, void* out, float sm_scale,
                      void* workspace, void* stream);
 
+/* mla_decode_mxfp4 for callers that cannot allocate device memory (code
+ * recorded into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument and no allocation of any kind. The plan
+ * words and split-K partials live in a static device array of the library
+ * (20 MiB, held by every GPU the library runs on until the process ends);
+ * the plan is built on the GPU from the device copy of kv_indptr ([batch+1]
+ * int32, 4-byte aligned), by the same rule and with the same items as
+ * mla_plan, so the output equals mla_decode_mxfp4's on a plan of the same
+ * offsets. q, kv_packed, kv_scale, out, sm_scale and stream as for
+ * mla_decode_mxfp4; kv_indptr may change in place between calls (up to
+ * 2^31 - 1 tokens). The array is shared by every call on a GPU and keeps
+ * the last call's contents: calls that overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.
+ *
+ * Errors (nothing enqueued): MLA_ERR_INVALID (batch < 0, non-finite
+ * sm_scale, null or misaligned pointer), MLA_ERR_WORKSPACE when the plan
+ * and partials of `batch` sequences exceed the static array (more than
+ * 129,885 sequences on a 256-CU device), MLA_ERR_DEVICE, MLA_ERR_HIP. */
+int mla_decode_mxfp4_noalloc(const void* q, const void* kv_packed, const void* kv_scale,
+                             const int32_t* kv_indptr, int32_t batch, void* out, float sm_scale,
+                             void* stream);
+
 /* The same decode over a cache whose rows are listed per token (page size
  * 1): sequence b reads rows kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1] of
  * the row pools kv_packed (uint8 [R, 288], 16-byte aligned) and kv_scale

@@ -29,6 +29,7 @@ EXPORTS = (
     "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
     "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
     "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts", "mla_decode_bf16_starts",
+    "mla_decode_mxfp4_noalloc",
 )
 
 _lib = None
@@ -66,6 +67,8 @@ def lib():
     L.mla_plan_release.argtypes = [ctypes.c_void_p]
     L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_mxfp4_noalloc.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                                                                   ctypes.c_void_p]
     L.mla_decode_mxfp4_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                                          ctypes.c_void_p]
@@ -91,7 +94,7 @@ def lib():
                  "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
                  "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
                  "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts",
-                 "mla_decode_bf16_starts"):
+                 "mla_decode_bf16_starts", "mla_decode_mxfp4_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -188,6 +191,16 @@ def decode(q, kv_packed, kv_scale, kv_indptr_dev, out, sm_scale: float, workspac
         ctypes.c_void_p(kv_scale.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale),
         ctypes.c_void_p(workspace.data_ptr()), _stream_ptr(stream)), "mla_decode_mxfp4")
+
+
+def decode_noalloc(q, kv_packed, kv_scale, kv_indptr_dev, batch: int, out, sm_scale: float, stream=None):
+    """Enqueue the decode that allocates nothing (plan and partials in the
+    library's static device array; the plan is built on the GPU from the
+    device offsets). Calls on one GPU share that array: order them."""
+    _check(lib().mla_decode_mxfp4_noalloc(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_packed.data_ptr()),
+        ctypes.c_void_p(kv_scale.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()), batch,
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale), _stream_ptr(stream)), "mla_decode_mxfp4_noalloc")
 
 
 def decode_mxfp4_paged(q, kv_packed, kv_scale, kv_indices, kv_indptr_dev, out, sm_scale: float, workspace,

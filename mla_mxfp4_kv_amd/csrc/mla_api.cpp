@@ -327,6 +327,67 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                        stream);
 }
 
+int mla_decode_mxfp4_noalloc(const void* q, const void* kv_packed, const void* kv_scale,
+                             const int32_t* kv_indptr, int32_t batch, void* out, float sm_scale,
+                             void* stream) {
+  if (batch < 0) return fail(MLA_ERR_INVALID, "batch must be >= 0");
+  if (!std::isfinite(sm_scale)) return fail(MLA_ERR_INVALID, "sm_scale must be finite");
+  if (kv_indptr == nullptr || !aligned(kv_indptr, 4))
+    return fail(MLA_ERR_INVALID, "kv_indptr must be a non-null 4-byte aligned device pointer");
+  if (batch > 0) {
+    if (q == nullptr || !aligned(q, 16)) return fail(MLA_ERR_INVALID, "q must be non-null and 16-byte aligned");
+    if (kv_packed == nullptr || !aligned(kv_packed, 16))
+      return fail(MLA_ERR_INVALID, "kv_packed must be non-null and 16-byte aligned");
+    if (kv_scale == nullptr) return fail(MLA_ERR_INVALID, "kv_scale must be non-null");
+    if (out == nullptr || !aligned(out, 16)) return fail(MLA_ERR_INVALID, "out must be non-null and 16-byte aligned");
+  }
+  int dev;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != MLA_OK) return st;
+  // the plan is laid out for any offsets of `batch` sequences (up to 2^31 - 1
+  // tokens), as mla_plan_device lays it out for its bounds
+  const mla::DeviceLayout l = mla::device_layout(batch, INT32_MAX, info.num_cus);
+  if ((size_t)l.total_bytes > mla::kNoAllocScratchBytes || l.off_out > INT32_MAX) {
+    char buf[200];
+    std::snprintf(buf, sizeof(buf),
+                  "batch %d needs %lld bytes of plan and partials; the static scratch holds %zu bytes",
+                  (int)batch, (long long)l.total_bytes, mla::kNoAllocScratchBytes);
+    return fail(MLA_ERR_WORKSPACE, buf);
+  }
+  void* ws = nullptr;
+  hipError_t e = (hipError_t)mla::noalloc_scratch(dev, &ws);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (batch == 0) return MLA_OK;
+  e = (hipError_t)mla::launch_plan_device(kv_indptr, batch, info.num_cus, INT32_MAX, l, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_plan_kernel launch");
+  mla::DecodeArgs a;
+  a.q = q;
+  a.kv_packed = (const uint8_t*)kv_packed;
+  a.kv_scale = (const uint8_t*)kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = nullptr;
+  a.page_indptr = nullptr;
+  a.page_size = 1;
+  a.kv_start = nullptr;
+  a.out = out;
+  a.plan = (const int32_t*)ws;
+  a.part_lse = (float*)((uint8_t*)ws + l.off_lse);
+  a.part_out = (float*)((uint8_t*)ws + l.off_out);
+  a.score_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.num_slots = (int32_t)l.slots;
+  a.num_reduce = batch;
+  // the counts are only known on the device (as for mla_plan_device)
+  a.wide_reduce = (int64_t)batch * 16 < l.slots ? 1 : 0;
+  const int gmax = info.num_cus * MLA_PLAN_WG_PER_CU;
+  a.grid = a.num_slots < gmax ? a.num_slots : gmax;
+  e = (hipError_t)mla::launch_decode(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_kernel launch");
+  e = (hipError_t)mla::launch_reduce(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_reduce_kernel launch");
+  return MLA_OK;
+}
+
 int mla_decode_mxfp4_paged(const void* q, const void* kv_packed, const void* kv_scale,
                            const int32_t* kv_indices, const int32_t* kv_indptr, void* out, float sm_scale,
                            void* workspace, void* stream) {

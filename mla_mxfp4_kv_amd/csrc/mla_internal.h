@@ -96,6 +96,12 @@ int launch_reduce(const DecodeArgs& a, void* stream);
 // of the fp8 per-tensor scale (unused for bf16).
 int launch_decode_dense(const DecodeArgs& a, bool fp8, const float* kv_scale, void* stream);
 
+// Static device scratch of mla_decode_mxfp4_noalloc (mla_noalloc.hip): its
+// size, and the device address of the current device's copy (looked up
+// once per device; returns the hipError_t as int).
+constexpr size_t kNoAllocScratchBytes = (size_t)20 << 20;
+int noalloc_scratch(int device, void** ptr);
+
 // Static LDS bytes the decode kernels need (for validation against the device).
 size_t decode_lds_bytes();
 size_t decode_dense_lds_bytes();
