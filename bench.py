@@ -68,6 +68,45 @@ def measured_traffic(workload: str, fmt: str = "mxfp4"):
         return None
 
 
+def profiled_kernel_us(workload: str, fmt: str = "mxfp4"):
+    """Average duration of the decode kernel in the committed rocprofv3 trace
+    summary of this workload, if it was taken on the current kernel source
+    (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{_profile_name(workload, fmt)}_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash(fmt):
+        return None
+    try:
+        return float(fields["decode_kernel_avg_us"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_probe_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Read bandwidth a plain device reduction over ``nbytes`` reaches on this
+    box (HIP events), the practical ceiling the decode's stream is compared
+    with."""
+    words = torch.ones(nbytes // 8, dtype=torch.int64, device="cuda")
+    words.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        words.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+    del words
+    return gbs
+
+
 def copy_probe(nbytes: int, reps: int) -> int:
     """Plain device-to-device copy of a known size (calibrates the
     FETCH_SIZE / WRITE_SIZE counters against bytes actually moved) and a
@@ -121,6 +160,11 @@ def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=Non
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = torch.get_num_threads()
+    cpu_count = os.cpu_count()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = cpu_count
     qb = q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     ind = [0]
     for n in lens:
@@ -153,6 +197,9 @@ def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=Non
         "value": round(gbs, 4),
         "unit": "GB/s",
         "cores": int(threads),
+        "cpu_count": cpu_count,
+        "affinity_cores": affinity,
+        "blas_threads": int(threads),
         "kind": "oracle",
         "sample": f"first {n_seq} of {len(lens)} sequences ({done_tokens} tokens) of {w.name} ({fmt} cache), "
                   f"{oracle_s:.1f} s, us/call extrapolated "
@@ -181,8 +228,14 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
-                    help="evict the L2/MALL by reading a 1 GB buffer before every timed call "
-                         "(a read leaves clean lines, so the decode does not pay for write-backs)")
+                    help="time the K steps with cold caches (a 1 GB read before every call evicts L2 and "
+                         "MALL; the read leaves clean lines, so the decode pays no write-backs). Without it "
+                         "the K steps run back to back and a cold pass of K calls is reported beside them")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed decode calls before the warm-up steps: a fresh process first "
+                         "runs through the GPU's clock/power transient (calls 2-8 fast, the next ~30 ~40%% "
+                         "slower, steady after ~300), which a short warm-up would otherwise time")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache pass")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args(argv)
@@ -307,8 +360,18 @@ def main(argv=None):
     else:
         def call():
             dec.bf16(q, packed, out=out, sm_scale=w.sm_scale)
-    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev) if args.cold else None
+    flush_buf = None if args.no_cold and not args.cold else torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    flush = flush_buf if args.cold else None
 
+    settle_calls = 0
+    if args.settle_s > 0:
+        print(f"[bench] settling clocks for {args.settle_s} s", file=sys.stderr, flush=True)
+        t_end = time.perf_counter() + args.settle_s
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                call()
+            settle_calls += 10
+            torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         call()
@@ -354,6 +417,32 @@ def main(argv=None):
     torch.cuda.synchronize()
     call_us = [a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)]
     med_us = statistics.median(call_us)
+    # the other cache state: cold calls beside a warm timed region, or
+    # back-to-back calls beside a cold one
+    other = None
+    if flush_buf is not None and not args.cold:
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush_buf.sum()
+            e0[i].record(stream)
+            call()
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in zip(e0, e1))
+        other = {"mode": "cold (1 GB read before each call)", "us_per_call_mean": round(statistics.fmean(cold_us), 2),
+                 "us_per_call_median": round(statistics.median(cold_us), 2),
+                 "us_p10_p90": [round(cold_us[int(0.1 * (len(cold_us) - 1))], 2),
+                                round(cold_us[int(0.9 * (len(cold_us) - 1))], 2)]}
+    elif args.cold:
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record(stream)
+        for _ in range(args.steps):
+            call()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        other = {"mode": "warm (back to back)", "us_per_call_mean": round(ea.elapsed_time(eb) * 1e3 / args.steps, 2)}
+    read_gbs = read_probe_gbs() if not args.groups else None
     ms_per_step = wall / args.steps * 1e3
     kvb = synth.kv_bytes(total, fmt)
     # whole-job throughput (wall clock over the timed steps); with --cold the
@@ -364,6 +453,7 @@ def main(argv=None):
                             page_table.page_indptr_host[-1] if page_table is not None else None)
     achieved = alg / (avg_us * 1e-6) / 1e9
 
+    prof_us = None if (args.gather or args.page_table or args.groups) else profiled_kernel_us(w.name, fmt)
     cpu = None
     if args.cpu_budget > 0 and not args.groups:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -387,7 +477,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"mxfp4": "bf16 (MXFP4 e2m1/E8M0 KV, fp32 accumulate)",
+        "dtype": {"mxfp4": "bf16 (MXFP4 e2m1/E8M0 KV; latent QK on the scaled fp4 x e4m3 MFMA, rope QK and "
+                           "P V on the bf16 MFMA, fp32 accumulate)",
                   "fp8": "bf16 (fp8 e4m3 KV + per-tensor scale, fp32 accumulate)",
                   "bf16": "bf16 (bf16 KV, fp32 accumulate)"}[fmt],
         "data": "synthetic",
@@ -421,7 +512,18 @@ def main(argv=None):
             "bytes_per_launch": alg,
             "kv_frac": round(kvb / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_source_sha256": kernel_source_hash(fmt),
+            # the event time covers the whole call: the decode kernel alone
+            # when no sequence is split (no reduce launch), else decode + reduce
+            "time_source": "HIP events on the decode stream, " + (
+                "decode kernel only (no reduce launch in this plan)" if words[10] == 0
+                else "decode + reduce kernels"),
+            "read_probe_gbs": round(read_gbs, 1) if read_gbs else None,
+            "frac_of_read_probe": round(achieved / read_gbs, 4) if read_gbs else None,
+            "profiled_kernel_us": prof_us,
+            "profiled_frac": round(alg / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if prof_us else None,
         },
+        "other_cache_state": other,
+        "clock_settle": {"seconds": args.settle_s, "calls": settle_calls},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
