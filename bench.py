@@ -29,9 +29,10 @@ KERNEL_SRC = {
     "mxfp4": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_kernels.hip"),
     "fp8": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
     "bf16": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_dense_kernels.hip"),
+    "mxfp4_24": os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_mxfp4_24_kernels.hip"),
 }
 KERNEL_NAME = {"mxfp4": "mla_decode_kernel<false, false, false>", "fp8": "mla_decode_dense_kernel<true, false>",
-               "bf16": "mla_decode_dense_kernel<false, false>"}
+               "bf16": "mla_decode_dense_kernel<false, false>", "mxfp4_24": "mla_decode_mxfp4_24_kernel"}
 GATHER_KERNEL_NAME = {"mxfp4": "mla_decode_kernel<true, false, false>", "fp8": "mla_decode_dense_kernel<true, true>",
                       "bf16": "mla_decode_dense_kernel<false, true>"}
 PAGE_TABLE_KERNEL_NAME = dict(GATHER_KERNEL_NAME, mxfp4="mla_decode_kernel<true, true, false>")
@@ -154,7 +155,7 @@ def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=Non
     """Time the fp64 oracle (as it stands) on whole sequences of the same
     workload until about ``budget_s`` seconds of CPU work."""
     import numpy as np
-    from oracle import dense_ref, mxfp4_ref
+    from oracle import dense_ref, mxfp4_24_ref, mxfp4_ref
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -174,11 +175,14 @@ def cpu_baseline(w, q, packed, scales, lens, budget_s, fmt="mxfp4", kv_scale=Non
     oracle_s = 0.0
     for b in range(len(lens)):
         lo, hi = ind[b], ind[b + 1]
-        if fmt == "mxfp4":
+        if fmt in ("mxfp4", "mxfp4_24"):
             pk = packed[lo:hi].cpu().numpy()
             sc = scales[lo:hi].cpu().numpy()
             t0 = time.perf_counter()          # device->host copies are not timed
-            mxfp4_ref.mla_decode_ref_seq(qb[b], pk, sc, w.sm_scale)
+            if fmt == "mxfp4":
+                mxfp4_ref.mla_decode_ref_seq(qb[b], pk, sc, w.sm_scale)
+            else:
+                mxfp4_24_ref.mla_decode_ref_24_seq(qb[b], pk, sc, w.sm_scale)
         elif fmt == "fp8":
             rows = packed[lo:hi].cpu().numpy()
             t0 = time.perf_counter()
@@ -213,8 +217,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="b256_kv8192", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--kv-format", default="mxfp4", choices=["mxfp4", "fp8", "bf16"],
-                    help="cache format: the MXFP4 headline path, or the fp8 / bf16 sibling decodes")
+    ap.add_argument("--kv-format", default="mxfp4", choices=["mxfp4", "fp8", "bf16", "mxfp4_24"],
+                    help="cache format: the MXFP4 headline path (18 scales per token), the 24-scale MXFP4 "
+                         "layout, or the fp8 / bf16 sibling decodes")
     ap.add_argument("--gather", type=int, default=0, metavar="PAGE",
                     help="scatter the rows over the pool in pages of PAGE rows (seeded shuffle) and "
                          "decode through per-token kv_indices (the *_paged entry points)")
@@ -256,8 +261,8 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     fmt = args.kv_format
     print(f"[bench] generating {w.name} ({fmt} cache)", file=sys.stderr, flush=True)
-    if fmt == "mxfp4":
-        q, packed, scales, indptr, lens = synth.make_inputs(w, device=dev)
+    if fmt in ("mxfp4", "mxfp4_24"):
+        q, packed, scales, indptr, lens = synth.make_inputs(w, device=dev, block=24 if fmt == "mxfp4_24" else 32)
         kv_scale_host = None
     else:
         # `packed` holds the cache rows, `scales` the fp8 per-tensor scale
@@ -354,6 +359,13 @@ def main(argv=None):
     elif fmt == "mxfp4":
         def call():
             dec(q, packed, scales, out=out, sm_scale=w.sm_scale)
+    elif fmt == "mxfp4_24":
+        if args.gather or args.page_table or args.groups:
+            print("the 24-scale layout is decoded from contiguous rows only", file=sys.stderr)
+            return 2
+
+        def call():
+            dec.mxfp4_24(q, packed, scales, out=out, sm_scale=w.sm_scale)
     elif fmt == "fp8":
         def call():
             dec.fp8(q, packed, scales, out=out, sm_scale=w.sm_scale)
@@ -461,6 +473,7 @@ def main(argv=None):
 
     line = {
         "metric": "KV-cache HBM GB/s (us/call), MXFP4 MLA decode" if fmt == "mxfp4"
+                  else "KV-cache HBM GB/s (us/call), MXFP4 (24 scales per token) MLA decode" if fmt == "mxfp4_24"
                   else f"KV-cache HBM GB/s (us/call), {fmt} MLA decode",
         "value": round(value, 2),
         "unit": "GB/s",
@@ -480,7 +493,9 @@ def main(argv=None):
         "dtype": {"mxfp4": "bf16 (MXFP4 e2m1/E8M0 KV; latent QK on the scaled fp4 x e4m3 MFMA, rope QK and "
                            "P V on the bf16 MFMA, fp32 accumulate)",
                   "fp8": "bf16 (fp8 e4m3 KV + per-tensor scale, fp32 accumulate)",
-                  "bf16": "bf16 (bf16 KV, fp32 accumulate)"}[fmt],
+                  "bf16": "bf16 (bf16 KV, fp32 accumulate)",
+                  "mxfp4_24": "bf16 (MXFP4 e2m1 KV with 24 E8M0 scales per token, decoded to bf16 for both "
+                              "bf16 MFMA products, fp32 accumulate)"}[fmt],
         "data": "synthetic",
         "cold": bool(args.cold),
         "config": {

@@ -55,6 +55,11 @@ extern "C" {
 #define MLA_SCALE_BLOCK 32
 #define MLA_PACKED_BYTES 288
 #define MLA_SCALES_PER_TOKEN 18
+/* The 24-scale layout (page "kernelbot-amd-mixed-mla-717900", mxfp4 layout
+ * comment block): 24 E8M0 bytes per token, byte k scaling elements
+ * 24k .. 24k+23. */
+#define MLA_SCALE_BLOCK_24 24
+#define MLA_SCALES_PER_TOKEN_24 24
 
 /* Planner constants: workgroups per compute unit, slot rounding, minimum
  * slot length in tokens. The plan rule is stated at mla_plan below. */
@@ -208,6 +213,21 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
 int mla_decode_mxfp4_noalloc(const void* q, const void* kv_packed, const void* kv_scale,
                              const int32_t* kv_indptr, int32_t batch, void* out, float sm_scale,
                              void* stream);
+
+/* The same decode over the 24-scale MXFP4 layout of page
+ * "kernelbot-amd-mixed-mla-717900" (mxfp4 layout comment block and the
+ * stage-1 loads of its Triton decode): kv_packed uint8 [T, 288] as for
+ * mla_decode_mxfp4 (element 2j the low nibble of byte j, e2m1 codes), and
+ * kv_scale uint8 [T, 24] (device, 8-byte aligned) whose byte k scales
+ * elements 24k .. 24k+23 (packed bytes 12k .. 12k+11) by 2^(byte-127); 255
+ * is NaN. V is again the first 512 decoded elements. The plan, workspace,
+ * q, kv_indptr, out, sm_scale, stream, ownership and error codes are those
+ * of mla_decode_mxfp4 (one plan serves every cache format), plus
+ * MLA_ERR_INVALID for a kv_scale that is not 8-byte aligned. The decoded
+ * elements are exact for scale bytes 2..252, as for the 18-scale layout. */
+int mla_decode_mxfp4_24(const void* q, const void* kv_packed, const void* kv_scale,
+                        const int32_t* kv_indptr, void* out, float sm_scale,
+                        void* workspace, void* stream);
 
 /* The same decode over a cache whose rows are listed per token (page size
  * 1): sequence b reads rows kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1] of

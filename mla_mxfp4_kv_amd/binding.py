@@ -29,7 +29,7 @@ EXPORTS = (
     "mla_decode_fp8", "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
     "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
     "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts", "mla_decode_bf16_starts",
-    "mla_decode_mxfp4_noalloc",
+    "mla_decode_mxfp4_noalloc", "mla_decode_mxfp4_24",
 )
 
 _lib = None
@@ -67,6 +67,7 @@ def lib():
     L.mla_plan_release.argtypes = [ctypes.c_void_p]
     L.mla_decode_mxfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_decode_mxfp4_24.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_mxfp4_noalloc.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
                                                                    ctypes.c_void_p]
     L.mla_decode_mxfp4_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -94,7 +95,7 @@ def lib():
                  "mla_decode_bf16", "mla_decode_mxfp4_paged", "mla_decode_fp8_paged",
                  "mla_decode_bf16_paged", "mla_decode_mxfp4_page_table", "mla_decode_fp8_page_table",
                  "mla_decode_bf16_page_table", "mla_decode_mxfp4_starts", "mla_decode_fp8_starts",
-                 "mla_decode_bf16_starts", "mla_decode_mxfp4_noalloc"):
+                 "mla_decode_bf16_starts", "mla_decode_mxfp4_noalloc", "mla_decode_mxfp4_24"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -330,6 +331,16 @@ def check_page_table(page_indices, page_indptr, kv_last_page_len, page_size: int
             raise ValueError("page_indices holds pages outside the pool")
 
 
+def decode_mxfp4_24(q, kv_packed, kv_scale24, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
+    """Enqueue the decode of the 24-scale MXFP4 cache (kv_scale24: uint8
+    [T, 24], 8-byte aligned)."""
+    _check(lib().mla_decode_mxfp4_24(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv_packed.data_ptr()),
+        ctypes.c_void_p(kv_scale24.data_ptr()), ctypes.c_void_p(kv_indptr_dev.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_float(sm_scale), ctypes.c_void_p(workspace.data_ptr()),
+        _stream_ptr(stream)), "mla_decode_mxfp4_24")
+
+
 def decode_fp8(q, kv_fp8, kv_scale, kv_indptr_dev, out, sm_scale: float, workspace, stream=None):
     """Enqueue the fp8-cache decode (``kv_scale``: float32 [1] device tensor)."""
     _check(lib().mla_decode_fp8(
@@ -377,6 +388,22 @@ class MlaDecode:
         if kv_packed.shape[0] < self.indptr_host[-1]:
             raise ValueError("kv_indptr reaches past the end of the cache rows")
         decode(q, kv_packed, kv_scale, self.kv_indptr, out, sm_scale, self.workspace, stream)
+        return out
+
+    def mxfp4_24(self, q, kv_packed, kv_scale24, out=None, sm_scale=1.0 / math.sqrt(576.0), stream=None):
+        """Decode over the 24-scale MXFP4 cache: kv_packed uint8 [T,288],
+        kv_scale24 uint8 [T,24] (byte k scales elements 24k..24k+23)."""
+        import torch
+        out = self._out(q, out)
+        if kv_packed.dtype != torch.uint8 or kv_packed.dim() != 2 or kv_packed.shape[1] != PACKED_BYTES \
+                or not kv_packed.is_contiguous():
+            raise ValueError("kv_packed must be contiguous uint8 [T,288]")
+        if kv_scale24.dtype != torch.uint8 or tuple(kv_scale24.shape) != (kv_packed.shape[0], 24) \
+                or not kv_scale24.is_contiguous():
+            raise ValueError("kv_scale24 must be contiguous uint8 [T,24]")
+        if kv_packed.shape[0] < self.indptr_host[-1]:
+            raise ValueError("kv_indptr reaches past the end of the cache rows")
+        decode_mxfp4_24(q, kv_packed, kv_scale24, self.kv_indptr, out, sm_scale, self.workspace, stream)
         return out
 
     def mxfp4_paged(self, q, kv_packed, kv_scale, kv_indices, out=None, sm_scale=1.0 / math.sqrt(576.0),

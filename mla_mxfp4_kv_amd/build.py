@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmla_mxfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["mla_api.cpp", "mla_plan.cpp", "mla_kernels.hip", "mla_dense_kernels.hip", "mla_plan_kernel.hip", "mla_noalloc.hip"]
+SOURCES = ["mla_api.cpp", "mla_plan.cpp", "mla_kernels.hip", "mla_dense_kernels.hip", "mla_plan_kernel.hip", "mla_noalloc.hip", "mla_mxfp4_24_kernels.hip"]
 
 # gfx950 only; packed-fp32 VALU forms are kept out of the generated code.
 HIP_FLAGS = [

@@ -64,7 +64,8 @@ int current_device(int* dev, DeviceInfo* info) {
   }
   *info = d;
   if (!d.is_gfx950) return fail(MLA_ERR_DEVICE, "the current HIP device is not gfx950 (MI355X)");
-  if (d.lds_per_block < mla::decode_lds_bytes() || d.lds_per_block < mla::decode_dense_lds_bytes())
+  if (d.lds_per_block < mla::decode_lds_bytes() || d.lds_per_block < mla::decode_dense_lds_bytes() ||
+      d.lds_per_block < mla::decode_24_lds_bytes())
     return fail(MLA_ERR_DEVICE, "device LDS per workgroup is smaller than the decode kernel needs");
   return MLA_OK;
 }
@@ -219,7 +220,7 @@ int mla_plan_release(void* workspace) {
 
 namespace {
 
-enum class KvFormat { kMxfp4, kFp8, kBf16 };
+enum class KvFormat { kMxfp4, kFp8, kBf16, kMxfp4_24 };
 
 // Shared validation and launch of the three cache formats: the plan, the
 // partial layout and the reduce kernel are the same for all of them.
@@ -251,10 +252,14 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   }
   if (pe.num_slots > 0) {
     if (q == nullptr || !aligned(q, 16)) return fail(MLA_ERR_INVALID, "q must be non-null and 16-byte aligned");
-    const char* kv_name = fmt == KvFormat::kMxfp4 ? "kv_packed" : fmt == KvFormat::kFp8 ? "kv_fp8" : "kv_bf16";
+    const char* kv_name = (fmt == KvFormat::kMxfp4 || fmt == KvFormat::kMxfp4_24) ? "kv_packed"
+                          : fmt == KvFormat::kFp8                                 ? "kv_fp8"
+                                                                                  : "kv_bf16";
     if (kv == nullptr || !aligned(kv, 16))
       return fail(MLA_ERR_INVALID, std::string(kv_name) + " must be non-null and 16-byte aligned");
     if (fmt == KvFormat::kMxfp4 && kv_scale == nullptr) return fail(MLA_ERR_INVALID, "kv_scale must be non-null");
+    if (fmt == KvFormat::kMxfp4_24 && (kv_scale == nullptr || !aligned(kv_scale, 8)))
+      return fail(MLA_ERR_INVALID, "kv_scale must be a non-null 8-byte aligned device pointer (24-scale rows)");
     if (gather) {
       if (kv_indices == nullptr || !aligned(kv_indices, 4))
         return fail(MLA_ERR_INVALID, "kv_indices must be a non-null 4-byte aligned device pointer");
@@ -288,6 +293,9 @@ int decode_common(KvFormat fmt, const void* q, const void* kv, const void* kv_sc
   if (fmt == KvFormat::kMxfp4) {
     e = (hipError_t)mla::launch_decode(a, stream);
     if (e != hipSuccess) return hip_fail(e, "mla_decode_kernel launch");
+  } else if (fmt == KvFormat::kMxfp4_24) {
+    e = (hipError_t)mla::launch_decode_24(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "mla_decode_mxfp4_24_kernel launch");
   } else {
     e = (hipError_t)mla::launch_decode_dense(a, fmt == KvFormat::kFp8, (const float*)kv_scale, stream);
     if (e != hipSuccess) return hip_fail(e, "mla_decode_dense_kernel launch");
@@ -324,6 +332,12 @@ int mla_decode_mxfp4(const void* q, const void* kv_packed, const void* kv_scale,
                      const int32_t* kv_indptr, void* out, float sm_scale, void* workspace,
                      void* stream) {
   return decode_common(KvFormat::kMxfp4, q, kv_packed, kv_scale, nullptr, kv_indptr, out, sm_scale, workspace,
+                       stream);
+}
+
+int mla_decode_mxfp4_24(const void* q, const void* kv_packed, const void* kv_scale, const int32_t* kv_indptr,
+                        void* out, float sm_scale, void* workspace, void* stream) {
+  return decode_common(KvFormat::kMxfp4_24, q, kv_packed, kv_scale, nullptr, kv_indptr, out, sm_scale, workspace,
                        stream);
 }
 

@@ -102,8 +102,13 @@ int launch_decode_dense(const DecodeArgs& a, bool fp8, const float* kv_scale, vo
 constexpr size_t kNoAllocScratchBytes = (size_t)20 << 20;
 int noalloc_scratch(int device, void** ptr);
 
+// 24-scale MXFP4 decode (mla_mxfp4_24_kernels.hip): a.kv_scale holds the
+// [T, 24] E8M0 rows (8-byte aligned); contiguous rows only.
+int launch_decode_24(const DecodeArgs& a, void* stream);
+
 // Static LDS bytes the decode kernels need (for validation against the device).
 size_t decode_lds_bytes();
 size_t decode_dense_lds_bytes();
+size_t decode_24_lds_bytes();
 
 }  // namespace mla

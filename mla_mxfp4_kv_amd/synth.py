@@ -63,21 +63,26 @@ WORKLOADS = {
 }
 
 
-def quantize_mxfp4(x: torch.Tensor):
+def quantize_mxfp4(x: torch.Tensor, block: int = 32):
     """MXFP4-encode rows of 576 values (any float dtype, any device).
 
-    Per 32-element block: shared exponent ``E = floor(log2(amax)) - 2``
+    Per ``block``-element block (32: 18 scales per token; 24: the 24-scale
+    layout of page "kernelbot-amd-mixed-mla-717900"): shared exponent
+    ``E = floor(log2(amax)) - 2``
     (exactly, from ``frexp``), stored as the E8M0 byte ``E + 127`` clamped to
     [0, 254]; an all-zero block stores 127. Each element ``x / 2^E`` is rounded
     to the nearest e2m1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the code
     with an even mantissa bit, saturating at 6; the sign bit is set for
     negative inputs. Codes are packed two per byte, element 2j in the low
-    nibble of byte j. Returns (packed uint8 [N, 288], scales uint8 [N, 18]).
+    nibble of byte j. Returns (packed uint8 [N, 288], scales uint8
+    [N, 576 / block]).
     """
     if x.dim() != 2 or x.shape[1] != QK_DIM:
         raise ValueError("x must be [N, 576]")
+    if block not in (24, 32):
+        raise ValueError("block must be 32 or 24")
     n = x.shape[0]
-    xd = x.to(torch.float64).reshape(n, SCALES_PER_TOKEN, 32)
+    xd = x.to(torch.float64).reshape(n, QK_DIM // block, block)
     amax = xd.abs().amax(dim=2)
     _, e = torch.frexp(amax)                     # amax = m * 2^e, m in [0.5, 1)
     byte = (e.to(torch.int32) - 3 + 127).clamp(0, 254)
@@ -133,17 +138,18 @@ def _draw(w: Workload, device, lengths):
     return lens, torch.tensor(indptr, dtype=torch.int32), total, q, rows()
 
 
-def make_inputs(w: Workload, device="cpu", lengths=None):
-    """Build (q bf16 [B,16,576], packed u8 [T,288], scales u8 [T,18],
+def make_inputs(w: Workload, device="cpu", lengths=None, block: int = 32):
+    """Build (q bf16 [B,16,576], packed u8 [T,288], scales u8 [T,576/block],
     kv_indptr int32 [B+1] on the host, lengths list) on ``device``.
 
-    ``lengths`` overrides the workload's length rule (for small test cases).
+    ``lengths`` overrides the workload's length rule (for small test cases);
+    ``block`` 24 gives the 24-scale cache of the same draws.
     """
     lens, kv_indptr, total, q, rows = _draw(w, device, lengths)
     packed = torch.empty(total, PACKED_BYTES, dtype=torch.uint8, device=q.device)
-    scales = torch.empty(total, SCALES_PER_TOKEN, dtype=torch.uint8, device=q.device)
+    scales = torch.empty(total, QK_DIM // block, dtype=torch.uint8, device=q.device)
     for r0, r1, x in rows:
-        pk, sc = quantize_mxfp4(x)
+        pk, sc = quantize_mxfp4(x, block)
         packed[r0:r1] = pk
         scales[r0:r1] = sc
     return q, packed, scales, kv_indptr, lens
@@ -188,11 +194,12 @@ def make_dense_inputs(w: Workload, fmt: str, device="cpu", lengths=None):
     return q, codes, scale, kv_indptr, lens
 
 
-KV_BYTES_PER_TOKEN = {"mxfp4": PACKED_BYTES + SCALES_PER_TOKEN, "fp8": QK_DIM, "bf16": 2 * QK_DIM}
+KV_BYTES_PER_TOKEN = {"mxfp4": PACKED_BYTES + SCALES_PER_TOKEN, "mxfp4_24": PACKED_BYTES + 24, "fp8": QK_DIM,
+                      "bf16": 2 * QK_DIM}
 
 
 def kv_bytes(total_tokens: int, fmt: str = "mxfp4") -> int:
     """Algorithmic KV-cache bytes a decode call must read: packed rows +
-    E8M0 scales (mxfp4, 306 B/token), fp8 rows (576 B/token; the one
+    E8M0 scales (mxfp4, 306 B/token; mxfp4_24, 312 B/token), fp8 rows (576 B/token; the one
     per-tensor scale is negligible) or bf16 rows (1152 B/token)."""
     return total_tokens * KV_BYTES_PER_TOKEN[fmt]

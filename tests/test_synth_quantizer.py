@@ -119,3 +119,27 @@ def test_workload_table():
     r = synth.seq_lengths(w["b128_ragged"])
     assert len(r) == 128 and min(r) >= 256 and max(r) <= 32768
     assert math.isclose(w["b4_kv1024"].sm_scale, 1 / 24)
+
+
+def test_24_element_blocks_follow_the_32_element_rule():
+    """quantize_mxfp4(x, 24) applies the same per-block rule to 24-element
+    blocks: each block, placed alone in the first 32-element block of an
+    otherwise zero row (zeros change no block max), gets the same codes and
+    scale byte from the already-pinned 32-element encoding."""
+    from mla_mxfp4_kv_amd import synth
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(6, 576, generator=g) * torch.exp2(torch.randint(-6, 7, (6, 1), generator=g).float()))
+    x[1, 24:48] = 0.0                     # an all-zero block
+    x = x.to(torch.bfloat16)
+    pk24, sc24 = synth.quantize_mxfp4(x, 24)
+    assert pk24.shape == (6, 288) and sc24.shape == (6, 24)
+    codes24 = torch.stack([pk24 & 15, pk24 >> 4], dim=2).reshape(6, 576)
+    for t in range(6):
+        for k in range(24):
+            row = torch.zeros(1, 576, dtype=torch.bfloat16)
+            row[0, :24] = x[t, 24 * k:24 * k + 24]
+            pk32, sc32 = synth.quantize_mxfp4(row, 32)
+            codes32 = torch.stack([pk32 & 15, pk32 >> 4], dim=2).reshape(576)
+            assert int(sc24[t, k]) == int(sc32[0, 0]), (t, k)
+            assert torch.equal(codes24[t, 24 * k:24 * k + 24], codes32[:24]), (t, k)
+    assert int(sc24[1, 1]) == 127 and int(codes24[1, 24:48].max()) == 0
