@@ -96,6 +96,7 @@ constexpr float kMInit = -1.0e30f;              // running max before the first 
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 static_assert(kTile * kRowBytes % 1024 == 0, "a tile's rows are whole 1 KB DMA instructions");
+static_assert(kRowDma + 1 < 16, "a tile's loads fit the low vmcnt field");
 
 // LDS layout by cache addressing. kGather (rows listed per token in
 // kv_indices) keeps each tile row's scale bytes in a 32-byte slot of its own
@@ -436,53 +437,124 @@ __device__ __forceinline__ void split16(const float* x, int sh, int* hi, int* lo
   }
 }
 
-// `sign` (0 or 0x80008000) is xored into every pair of bf16 values: a
-// negative softmax scale is applied as |scale| on -q, which is exact.
-__device__ __forceinline__ QOperands load_q(const uint16_t* qh, int grp, uint32_t sign) {
+// The q operands are built once per item by the four scorer waves together:
+// wave `pair` loads and splits the 128-dim chunk m = pair for all 16 heads
+// and leaves it in LDS, then every scorer reads all four chunks back. The
+// lane's pieces of chunk m as loaded: 4 x 16 bytes (and the 64 rope dims,
+// which every scorer loads for itself).
+struct QChunk {
+  u32x4_t w[4];
+  u32x4_t rope[2];
+};
+
+__device__ __forceinline__ QChunk load_q_chunk(const uint16_t* qh, int m, int grp) {
+  QChunk c;
+  const u32x4_t* p0 = (const u32x4_t*)(qh + 128 * m + 16 * grp);
+  const u32x4_t* p1 = (const u32x4_t*)(qh + 128 * m + 64 + 16 * grp);
+  c.w[0] = p0[0];
+  c.w[1] = p0[1];
+  c.w[2] = p1[0];
+  c.w[3] = p1[1];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) c.rope[s] = *(const u32x4_t*)(qh + 512 + 16 * grp + 8 * s);
+  return c;
+}
+
+// Split of one chunk: the e4m3 hi and lo operands and the lane's E8M0 byte
+// of each. `sign` (0 or 0x80008000) is xored into every pair of bf16 values:
+// a negative softmax scale is applied as |scale| on -q, which is exact.
+__device__ __forceinline__ void split_chunk(const QChunk& c, int grp, uint32_t sign, i32x8_t& fhi, i32x8_t& flo,
+                                            uint32_t& sc_hi, uint32_t& sc_lo) {
+  const u32x4_t w[4] = {c.w[0] ^ sign, c.w[1] ^ sign, c.w[2] ^ sign, c.w[3] ^ sign};
+  float x[32];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[8 * v + 2 * k] = bf16_lo(w[v][k]);
+      x[8 * v + 2 * k + 1] = bf16_hi(w[v][k]);
+    }
+  float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    m0 = fmaxf(m0, fabsf(x[k]));
+    m1 = fmaxf(m1, fabsf(x[16 + k]));
+  }
+  // The other half of blocks grp/2 and 2 + grp/2 sits in lane group grp ^ 1.
+  m0 = fmaxf(m0, __shfl_xor(m0, 16));
+  m1 = fmaxf(m1, __shfl_xor(m1, 16));
+  const int s0 = e8m0_for_max(m0);   // block grp/2
+  const int s1 = e8m0_for_max(m1);   // block 2 + grp/2
+  int hi[8], lo[8];
+  split16(x, s0, hi, lo);
+  split16(x + 16, s1, hi + 4, lo + 4);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    fhi[d] = hi[d];
+    flo[d] = lo[d];
+  }
+  // Block grp's scale: own s0 (grp 0), own s1 (grp 3), else lane group grp ^ 2's.
+  const int o0 = __shfl_xor(s0, 32), o1 = __shfl_xor(s1, 32);
+  const int sup = grp == 0 ? s0 : grp == 3 ? s1 : grp == 1 ? o0 : o1;
+  sc_hi = (uint32_t)sup;
+  sc_lo = (uint32_t)max(sup - 4, 0);
+}
+
+// LDS staging of the split chunks (in the hand-off area, free until round
+// 0): [chunk][hi | lo][lane] 32-byte slots, then [hi | lo][lane] dwords of
+// E8M0 bytes (byte m = chunk m). Written and read with inline assembly, so
+// that the compiler does not hold them behind the tile loads in flight;
+// the writes are complete at the barrier between (see stage_q / fetch_q).
+constexpr int kQStage = 4 * 2 * 64 * 32;                   // 16 KB
+static_assert(kQStage == 2 * kPairs * 64 * 32, "the q stage fills the hand-off area");
+
+__device__ __forceinline__ void stage_q(uint8_t* stage, uint8_t* stage_sc, int m, int lane, const i32x8_t& hi,
+                                        const i32x8_t& lo, uint32_t sc_hi, uint32_t sc_lo) {
+  const uint32_t a = lds_addr(stage + (m * 2 * 64 + lane) * 32);
+  const u32x4_t h0 = {(uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
+  const u32x4_t h1 = {(uint32_t)hi[4], (uint32_t)hi[5], (uint32_t)hi[6], (uint32_t)hi[7]};
+  const u32x4_t l0 = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3]};
+  const u32x4_t l1 = {(uint32_t)lo[4], (uint32_t)lo[5], (uint32_t)lo[6], (uint32_t)lo[7]};
+  asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:16\n\t"
+               "ds_write_b128 %0, %3 offset:2048\n\tds_write_b128 %0, %4 offset:2064"
+               ::"v"(a), "v"(h0), "v"(h1), "v"(l0), "v"(l1) : "memory");
+  const uint32_t sa = lds_addr(stage_sc + 4 * lane + m);
+  asm volatile("ds_write_b8 %0, %1\n\tds_write_b8 %0, %2 offset:256" ::"v"(sa), "v"(sc_hi), "v"(sc_lo)
+               : "memory");
+}
+
+__device__ __forceinline__ QOperands fetch_q(const uint8_t* stage, const uint8_t* stage_sc, int lane,
+                                             const QChunk& own, uint32_t sign) {
   QOperands f;
-  f.sc_hi = 0u;
-  f.sc_lo = 0u;
+  u32x4_t r[16];
+  const uint32_t a = lds_addr(stage + lane * 32);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const u32x4_t* p0 = (const u32x4_t*)(qh + 128 * m + 16 * grp);
-    const u32x4_t* p1 = (const u32x4_t*)(qh + 128 * m + 64 + 16 * grp);
-    const u32x4_t w[4] = {p0[0] ^ sign, p0[1] ^ sign, p1[0] ^ sign, p1[1] ^ sign};
-    float x[32];
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * v + 2 * k] = bf16_lo(w[v][k]);
-        x[8 * v + 2 * k + 1] = bf16_hi(w[v][k]);
-      }
-    float m0 = 0.f, m1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      m0 = fmaxf(m0, fabsf(x[k]));
-      m1 = fmaxf(m1, fabsf(x[16 + k]));
-    }
-    // The other half of blocks grp/2 and 2 + grp/2 sits in lane group grp ^ 1.
-    m0 = fmaxf(m0, __shfl_xor(m0, 16));
-    m1 = fmaxf(m1, __shfl_xor(m1, 16));
-    const int s0 = e8m0_for_max(m0);   // block grp/2
-    const int s1 = e8m0_for_max(m1);   // block 2 + grp/2
-    int hi[8], lo[8];
-    split16(x, s0, hi, lo);
-    split16(x + 16, s1, hi + 4, lo + 4);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      f.hi[m][d] = hi[d];
-      f.lo[m][d] = lo[d];
-    }
-    // Block grp's scale: own s0 (grp 0), own s1 (grp 3), else lane group grp ^ 2's.
-    const int o0 = __shfl_xor(s0, 32), o1 = __shfl_xor(s1, 32);
-    const int sup = grp == 0 ? s0 : grp == 3 ? s1 : grp == 1 ? o0 : o1;
-    f.sc_hi |= (uint32_t)sup << (8 * m);
-    f.sc_lo |= (uint32_t)max(sup - 4, 0) << (8 * m);
+    // chunk m: hi at m * 4096, lo 2048 further
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r[4 * m + 0]) : "v"(a), "i"(m * 4096));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r[4 * m + 1]) : "v"(a), "i"(m * 4096 + 16));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r[4 * m + 2]) : "v"(a), "i"(m * 4096 + 2048));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r[4 * m + 3]) : "v"(a), "i"(m * 4096 + 2064));
   }
+  uint32_t sh, sl;
+  const uint32_t sa = lds_addr(stage_sc + 4 * lane);
+  asm volatile("ds_read_b32 %0, %1" : "=v"(sh) : "v"(sa));
+  asm volatile("ds_read_b32 %0, %1 offset:256" : "=v"(sl) : "v"(sa));
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]),
+                 "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]), "+v"(r[14]),
+                 "+v"(r[15]), "+v"(sh), "+v"(sl));
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-    f.rope[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qh + 512 + 16 * grp + 8 * s) ^ sign);
+  for (int m = 0; m < 4; ++m) {
+    f.hi[m] = i32x8_t{(int)r[4 * m][0], (int)r[4 * m][1], (int)r[4 * m][2], (int)r[4 * m][3],
+                      (int)r[4 * m + 1][0], (int)r[4 * m + 1][1], (int)r[4 * m + 1][2], (int)r[4 * m + 1][3]};
+    f.lo[m] = i32x8_t{(int)r[4 * m + 2][0], (int)r[4 * m + 2][1], (int)r[4 * m + 2][2], (int)r[4 * m + 2][3],
+                      (int)r[4 * m + 3][0], (int)r[4 * m + 3][1], (int)r[4 * m + 3][2], (int)r[4 * m + 3][3]};
+  }
+  f.sc_hi = sh;
+  f.sc_lo = sl;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) f.rope[s] = __builtin_bit_cast(bf16x8_t, own.rope[s] ^ sign);
   return f;
 }
 
@@ -679,18 +751,37 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
+  // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
+  // (kv_start), consecutive slots -- the query groups of one sequence --
+  // go to workgroups of one XCD, so that its L2 serves the repeated reads.
+  const bool xcd_order = kStarts && (gridDim.x & 7) == 0;
+  const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                   : (int)blockIdx.x;
+  // The header words and the first slot's bounds in slot_indptr (which
+  // both planners place right after the header, and which has an entry for
+  // every launched workgroup) are read in one batch, before the check: a
+  // memory latency each saved on the way to the first tile.
+  const int32_t* slot_indptr = plan + MLA_PLAN_HEADER_WORDS;
+  const int magic = plan[kPwMagic];
+  const int version = plan[kPwVersion];
+  const int num_slots = plan[kPwNumSlots];
+  const int off_items = plan[kPwOffItems];
+  int i_begin = slot_indptr[first_slot];
+  int i_end = slot_indptr[first_slot + 1];
+  // (the compiler would otherwise load each only where it is first used,
+  // one latency after another; the kernel arguments are fetched here too)
+  asm volatile("" ::"s"(num_slots), "s"(off_items), "s"(i_begin), "s"(i_end), "s"(q), "s"(kv), "s"(sc),
+               "s"(kv_indptr), "s"(out));
   // Only words written by a planner are followed: a workspace whose header
   // is not a plan of this version (never planned, overwritten, or an
   // empty device plan) leaves the output untouched.
-  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
+  if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
   // A negative scale is applied as |scale| on -q (exact), so the running
   // max below is a max of the scaled scores whatever the scale's sign.
   const uint32_t qsign = csc < 0.f ? 0x80008000u : 0u;
   csc = fabsf(csc);
 
-  const int num_slots = plan[kPwNumSlots];
-  const int32_t* slot_indptr = plan + plan[kPwOffSlot];
-  const int32_t* items = plan + plan[kPwOffItems];
+  const int32_t* items = plan + off_items;
   uint8_t* ring = lds + pair * L::kPair;
   TileHandoff* hand = (TileHandoff*)(lds + L::kXchg) + pair * 64 + lane;  // + parity * kPairs * 64
   uint8_t* fmt_pair = lds + L::kFmt + pair * kFmtTile;  // + parity * kPairs * kFmtTile
@@ -698,15 +789,11 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // priority over the P V wave on the shared SIMD.
   if (scorer) __builtin_amdgcn_s_setprio(1);
 
-  // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
-  // (kv_start), consecutive slots -- the query groups of one sequence --
-  // go to workgroups of one XCD, so that its L2 serves the repeated reads.
-  const bool xcd_order = kStarts && (gridDim.x & 7) == 0;
-  const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
-                                   : (int)blockIdx.x;
   for (int slot = first_slot; slot < num_slots; slot += gridDim.x) {
-    const int i_begin = slot_indptr[slot];
-    const int i_end = slot_indptr[slot + 1];
+    if (slot != first_slot) {
+      i_begin = slot_indptr[slot];
+      i_end = slot_indptr[slot + 1];
+    }
     for (int it = i_begin; it < i_end; ++it) {
       const int b = items[4 * it + 0];
       const int seq_lo = kv_indptr[b];
@@ -749,7 +836,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         SoftmaxState st;
         st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
         st.m = kMInit;
-        const QOperands qo = load_q(q + ((size_t)b * kHeads + col) * kQkDim, grp, qsign);
+        const QChunk qc = load_q_chunk(q + ((size_t)b * kHeads + col) * kQkDim, pair, grp);
         PageRows pages = {0u, 0u};   // page tables: the entries of the next tile to stage
         __syncthreads();  // LDS of the previous item's merge is free again
         if (ntiles > 0) {
@@ -772,6 +859,23 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
             stage_dma(ring, kv_b, sc_b, t_first, ke - t_first, lane);
           }
         }
+        // This wave's chunk of q is split while tile 0 is in flight: only the
+        // q loads, older than the tile's kRowDma + 1 loads, are waited for.
+        if constexpr (!kGather) {
+          if (ntiles > 0)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (kRowDma + 1));   // vmcnt(kRowDma + 1)
+          else
+            __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0)
+        }
+        {
+          i32x8_t qhi, qlo;
+          uint32_t qsh, qsl;
+          split_chunk(qc, grp, qsign, qhi, qlo, qsh, qsl);
+          stage_q(lds + L::kXchg, lds + L::kFmt, pair, lane, qhi, qlo, qsh, qsl);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();  // all four chunks staged
+        const QOperands qo = fetch_q(lds + L::kXchg, lds + L::kFmt, lane, qc, qsign);
         for (int i = 0; i <= rounds; ++i) {
           const bool qk_on = i < ntiles;
           if (qk_on) wait_dma();
@@ -822,6 +926,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 #pragma unroll
         for (int n = 0; n < 32; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
+        __syncthreads();  // (the scorers stage q between the two)
         for (int i = 0; i <= rounds; ++i) {
           __syncthreads();
           if (i >= 1 && i - 1 < ntiles) {
@@ -1018,17 +1123,29 @@ mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restri
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  // partials in order, four at a time with all their loads in flight
+  constexpr int kUnroll = 4;
   f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
   float wsum = 0.f;
-  for (int i = 0; i < cnt; ++i) {
-    const float v = part_lse[(size_t)(first + i) * kHeads + h];
-    const f32x4_t* src = (const f32x4_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + d);
-    const f32x4_t o0 = src[0], o1 = src[1];
-    if (v != kNegInf) {
-      const float w = __builtin_amdgcn_exp2f(v - m);
-      wsum += w;
-      a0 += w * o0;
-      a1 += w * o1;
+  for (int i0 = 0; i0 < cnt; i0 += kUnroll) {
+    float v[kUnroll];
+    f32x4_t o0[kUnroll], o1[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = min(i0 + u, cnt - 1);
+      v[u] = part_lse[(size_t)(first + i) * kHeads + h];
+      const f32x4_t* src = (const f32x4_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + d);
+      o0[u] = src[0];
+      o1[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (i0 + u < cnt && v[u] != kNegInf) {
+        const float w = __builtin_amdgcn_exp2f(v[u] - m);
+        wsum += w;
+        a0 += w * o0[u];
+        a1 += w * o1[u];
+      }
     }
   }
   const float inv = wsum != 0.f ? 1.0f / wsum : 0.f;
