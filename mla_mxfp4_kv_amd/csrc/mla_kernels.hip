@@ -1004,21 +1004,33 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 // LSE-weighted merge of the partials of one sequence (or zero fill of an
 // empty one), for plans with long splits (many partials per sequence):
 // out = sum_p 2^(lse_p - M) O_p / sum_p 2^(lse_p - M) with M = max_p lse_p
-// over non-empty partials (each wave uses its own running max, the waves'
-// sums are rescaled to the common one when merged). One workgroup per
-// (reduce entry, head, quarter of the 512 dims); its 16 waves take every
-// 16th partial (so a long split sequence is merged by many waves with their
-// loads in flight) and are summed through LDS. Lane covers 2 consecutive
-// output dims.
+// over non-empty partials. One workgroup per (reduce entry, head, 32-dim
+// slice), so that a single long sequence still spreads its partials' reads
+// over 256 workgroups. Its 16 waves x 4 lane groups are 64 streams, stream s
+// taking partials s, s + 64, ...; a lane group's 16 lanes cover the slice's
+// 32 dims two each. Every stream keeps a running max and rescales its sums
+// when it rises; the streams are combined by shuffles within the wave, then
+// through LDS across the waves.
 constexpr int kReduceWaves = 16;
 constexpr int kReduceThreads = 64 * kReduceWaves;
-constexpr int kReduceSplit = 4;                      // dim quarters per head
-static_assert(kVDim / kReduceSplit == 2 * 64, "reduce: a wave covers one quarter of the dims");
+constexpr int kReduceSplit = 16;                     // 32-dim slices per head
+constexpr int kReduceStreams = 4 * kReduceWaves;     // 4 lane groups per wave
+static_assert(kVDim / kReduceSplit == 2 * 16, "reduce: a lane group covers one slice, two dims per lane");
+
+// (m, s, a) <- the merge of two running states (m = -inf: empty)
+__device__ __forceinline__ void merge_state(float& m, float& s, f32x2_t& a, float m2, float s2, f32x2_t a2) {
+  const float mm = fmaxf(m, m2);
+  const float f1 = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+  const float f2 = m2 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+  s = s * f1 + s2 * f2;
+  a = a * f1 + a2 * f2;
+  m = mm;
+}
 
 __global__ void __launch_bounds__(kReduceThreads)
 mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
                   const float* __restrict__ part_out, uint16_t* __restrict__ out) {
-  __shared__ f32x2_t acc_s[kReduceWaves][64];
+  __shared__ f32x2_t acc_s[kReduceWaves][16];
   __shared__ float wsum_s[kReduceWaves];
   __shared__ float max_s[kReduceWaves];
   // a plan built on the GPU is launched for its bound on the entry count
@@ -1029,33 +1041,32 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
   const int first = ent[1];
   const int cnt = ent[2];
   const int h = blockIdx.y;
-  const int d = (kVDim / kReduceSplit) * blockIdx.z + 2 * (threadIdx.x & 63);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int d = (kVDim / kReduceSplit) * blockIdx.z + 2 * l16;
   uint32_t* dst = (uint32_t*)(out + ((size_t)b * kHeads + h) * kVDim + d);
   if (cnt == 0) {
-    if (wave == 0) *dst = 0u;
+    if (wave == 0 && lane < 16) *dst = 0u;
     return;
   }
-  // One pass: each wave keeps a running max over its partials (every 16th,
-  // eight loads in flight) and rescales its sums when the max rises; the 16
-  // waves' (max, sums) are then merged through LDS.
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = 4;
   float m = kNegInf;
   f32x2_t acc = {0.f, 0.f};
   float wsum = 0.f;
-  for (int i0 = wave; i0 < cnt; i0 += kUnroll * kReduceWaves) {
+  const int stream = 4 * wave + (lane >> 4);
+  for (int i0 = stream; i0 < cnt; i0 += kUnroll * kReduceStreams) {
     float v[kUnroll];
     f32x2_t o[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int i = min(i0 + u * kReduceWaves, cnt - 1);
+      const int i = min(i0 + u * kReduceStreams, cnt - 1);
       v[u] = part_lse[(size_t)(first + i) * kHeads + h];
       o[u] = *(const f32x2_t*)(part_out + ((size_t)(first + i) * kHeads + h) * kVDim + d);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (i0 + u * kReduceWaves < cnt && v[u] != kNegInf) {
+      if (i0 + u * kReduceStreams < cnt && v[u] != kNegInf) {
         const float m_new = fmaxf(m, v[u]);
         const float keep = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
         const float w = __builtin_amdgcn_exp2f(v[u] - m_new);
@@ -1065,13 +1076,21 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
       }
     }
   }
-  acc_s[wave][lane] = acc;
+  // the wave's 4 lane groups (same dims, other partials)
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float s2 = __shfl_xor(wsum, off);
+    const f32x2_t a2 = {__shfl_xor(acc[0], off), __shfl_xor(acc[1], off)};
+    merge_state(m, wsum, acc, m2, s2, a2);
+  }
+  if (lane < 16) acc_s[wave][lane] = acc;
   if (lane == 0) {
     wsum_s[wave] = wsum;
     max_s[wave] = m;
   }
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 0 && lane < 16) {
     float mm = kNegInf;
 #pragma unroll
     for (int w = 0; w < kReduceWaves; ++w) mm = fmaxf(mm, max_s[w]);
