@@ -1033,10 +1033,16 @@ mla_reduce_kernel(const int32_t* __restrict__ plan, const float* __restrict__ pa
   __shared__ f32x2_t acc_s[kReduceWaves][16];
   __shared__ float wsum_s[kReduceWaves];
   __shared__ float max_s[kReduceWaves];
-  // a plan built on the GPU is launched for its bound on the entry count
-  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
-  if ((int)blockIdx.x >= plan[kPwNumReduce]) return;
-  const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
+  // header words in one batch; a plan built on the GPU is launched for its
+  // bound on the entry count
+  const int magic = plan[kPwMagic];
+  const int version = plan[kPwVersion];
+  const int num_reduce = plan[kPwNumReduce];
+  const int off_reduce = plan[kPwOffReduce];
+  asm volatile("" ::"s"(num_reduce), "s"(off_reduce), "s"(part_lse), "s"(part_out), "s"(out));
+  if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
+  if ((int)blockIdx.x >= num_reduce) return;
+  const int32_t* ent = plan + off_reduce + 4 * blockIdx.x;
   const int b = ent[0];
   const int first = ent[1];
   const int cnt = ent[2];
@@ -1121,9 +1127,16 @@ static_assert(kVDim == 8 * kNarrowThreads, "narrow reduce: a lane covers 8 dims"
 __global__ void __launch_bounds__(kNarrowThreads)
 mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restrict__ part_lse,
                          const float* __restrict__ part_out, uint16_t* __restrict__ out) {
-  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
-  if ((int)blockIdx.x >= plan[kPwNumReduce]) return;
-  const int32_t* ent = plan + plan[kPwOffReduce] + 4 * blockIdx.x;
+  // header words in one batch (the compiler would fetch each after the
+  // previous check), then the entry
+  const int magic = plan[kPwMagic];
+  const int version = plan[kPwVersion];
+  const int num_reduce = plan[kPwNumReduce];
+  const int off_reduce = plan[kPwOffReduce];
+  asm volatile("" ::"s"(num_reduce), "s"(off_reduce), "s"(part_lse), "s"(part_out), "s"(out));
+  if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
+  if ((int)blockIdx.x >= num_reduce) return;
+  const int32_t* ent = plan + off_reduce + 4 * blockIdx.x;
   const int b = ent[0];
   const int first = ent[1];
   const int cnt = ent[2];
@@ -1135,20 +1148,12 @@ mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restri
     *dst = u32x4_t{0u, 0u, 0u, 0u};
     return;
   }
-  float m = kNegInf;
-  for (int i = lane; i < cnt; i += kNarrowThreads) {
-    const float v = part_lse[(size_t)(first + i) * kHeads + h];
-    if (v != kNegInf) m = fmaxf(m, v);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  // partials in order, four at a time with all their loads in flight
+  // partials in order, four at a time with all their loads in flight; the
+  // first four go out together with the LSE loads of the max
   constexpr int kUnroll = 4;
-  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  float wsum = 0.f;
-  for (int i0 = 0; i0 < cnt; i0 += kUnroll) {
-    float v[kUnroll];
-    f32x4_t o0[kUnroll], o1[kUnroll];
+  float v[kUnroll];
+  f32x4_t o0[kUnroll], o1[kUnroll];
+  auto load_batch = [&](int i0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i = min(i0 + u, cnt - 1);
@@ -1157,6 +1162,19 @@ mla_reduce_narrow_kernel(const int32_t* __restrict__ plan, const float* __restri
       o0[u] = src[0];
       o1[u] = src[1];
     }
+  };
+  load_batch(0);
+  float m = kNegInf;
+  for (int i = lane; i < cnt; i += kNarrowThreads) {
+    const float x = part_lse[(size_t)(first + i) * kHeads + h];
+    if (x != kNegInf) m = fmaxf(m, x);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  float wsum = 0.f;
+  for (int i0 = 0; i0 < cnt; i0 += kUnroll) {
+    if (i0 > 0) load_batch(i0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (i0 + u < cnt && v[u] != kNegInf) {
