@@ -241,6 +241,10 @@ def main(argv=None):
                          "runs through the GPU's clock/power transient (calls 2-8 fast, the next ~30 ~40%% "
                          "slower, steady after ~300), which a short warm-up would otherwise time")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache pass")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps as one HIP-graph replay of K captured calls (no host launch cost "
+                         "between calls: what a serving loop that replays graphs sees); without it the calls "
+                         "are launched from Python one by one, which bounds small workloads by the host")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args(argv)
@@ -393,7 +397,35 @@ def main(argv=None):
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    if flush is None:
+    graph = None
+    if args.graph:
+        if flush is not None:
+            print("--graph and --cold are exclusive", file=sys.stderr)
+            return 2
+        # capture on a side stream (the decode launches on the current stream)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                call()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+    if graph is not None:
+        ev_a = torch.cuda.Event(enable_timing=True)
+        ev_b = torch.cuda.Event(enable_timing=True)
+        ev_a.record(stream)
+        graph.replay()
+        ev_b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        avg_us = ev_a.elapsed_time(ev_b) * 1e3 / args.steps
+    elif flush is None:
         # back-to-back calls, one event pair around the whole timed region
         ev_a = torch.cuda.Event(enable_timing=True)
         ev_b = torch.cuda.Event(enable_timing=True)
@@ -498,6 +530,8 @@ def main(argv=None):
                               "bf16 MFMA products, fp32 accumulate)"}[fmt],
         "data": "synthetic",
         "cold": bool(args.cold),
+        "timing": "HIP-graph replay of the K calls" if args.graph else
+                  ("per-call event pairs, cold caches" if args.cold else "back-to-back calls launched from Python"),
         "config": {
             "workload": w.name,
             "kv_format": fmt,

@@ -498,17 +498,24 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
+  // Header words in one batch (the compiler would fetch each only after the
+  // previous check, a memory latency apiece).
+  const int magic = plan[kPwMagic];
+  const int version = plan[kPwVersion];
+  const int num_slots = plan[kPwNumSlots];
+  const int off_slot = plan[kPwOffSlot];
+  const int off_items = plan[kPwOffItems];
+  asm volatile("" ::"s"(num_slots), "s"(off_slot), "s"(off_items), "s"(q), "s"(kv), "s"(kv_indptr), "s"(out));
   // Only words written by a planner are followed: a workspace whose header
   // is not a plan of this version leaves the output untouched.
-  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
+  if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
   // V scale and base-2 logit scale: the per-tensor fp8 scale multiplies both
   float vs = 1.0f;
   if constexpr (kFp8) vs = kv_scale[0];
   const float sc2 = csc * vs;
 
-  const int num_slots = plan[kPwNumSlots];
-  const int32_t* slot_indptr = plan + plan[kPwOffSlot];
-  const int32_t* items = plan + plan[kPwOffItems];
+  const int32_t* slot_indptr = plan + off_slot;
+  const int32_t* items = plan + off_items;
   uint8_t* ring = lds + wave * (2 * kTileBytes);   // this wave's two tile buffers
   // merge area, over the tile buffers once every wave is done: the O tiles
   // of all waves, then the (m, l) statistics

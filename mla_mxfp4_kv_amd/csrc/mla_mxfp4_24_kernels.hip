@@ -330,12 +330,19 @@ mla_decode_mxfp4_24_kernel(const uint16_t* __restrict__ q, const uint8_t* __rest
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  // only words written by a planner are followed
-  if (plan[kPwMagic] != MLA_PLAN_MAGIC || plan[kPwVersion] != MLA_PLAN_VERSION) return;
-
+  // header words in one batch (the compiler would fetch each only after the
+  // previous check); only words written by a planner are followed
+  const int magic = plan[kPwMagic];
+  const int version = plan[kPwVersion];
   const int num_slots = plan[kPwNumSlots];
-  const int32_t* slot_indptr = plan + plan[kPwOffSlot];
-  const int32_t* items = plan + plan[kPwOffItems];
+  const int off_slot = plan[kPwOffSlot];
+  const int off_items = plan[kPwOffItems];
+  asm volatile("" ::"s"(num_slots), "s"(off_slot), "s"(off_items), "s"(q), "s"(kv), "s"(sc), "s"(kv_indptr),
+               "s"(out));
+  if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
+
+  const int32_t* slot_indptr = plan + off_slot;
+  const int32_t* items = plan + off_items;
   uint8_t* ring = lds + wave * kWaveLds;
   uint8_t* fmt = ring + kNumBuf * kBuf;
   f32x4_t* frag = (f32x4_t*)lds;
