@@ -62,10 +62,13 @@ extern "C" {
 #define MLA_SCALES_PER_TOKEN_24 24
 
 /* Planner constants: workgroups per compute unit, slot rounding, minimum
- * slot length in tokens. The plan rule is stated at mla_plan below. */
+ * slot length in tokens, and the fixed work of one item (its Q, its first
+ * tile, the merge and stores) in tokens of streaming. The plan rule is
+ * stated at mla_plan below. */
 #define MLA_PLAN_WG_PER_CU 1
 #define MLA_PLAN_CHUNK_ALIGN 128
 #define MLA_PLAN_MIN_CHUNK 256
+#define MLA_PLAN_ITEM_COST 512
 #define MLA_PLAN_MAGIC 0x4D4C4134
 #define MLA_PLAN_VERSION 1
 #define MLA_PLAN_HEADER_WORDS 16
@@ -107,11 +110,18 @@ int mla_workspace_bytes(int32_t batch, int64_t total_kv, int32_t num_cus, size_t
  * "kernelbot-amd-mixed-mla-608791", host metadata builder, gives the role of
  * the work list and per-batch partial index): with T = kv_indptr[B] -
  * kv_indptr[0] tokens and G = num_cus * MLA_PLAN_WG_PER_CU workgroups,
- * chunk = max(MLA_PLAN_MIN_CHUNK, round_up(ceil(T/G), MLA_PLAN_CHUNK_ALIGN)),
- * and slot s owns the contiguous tokens [s*chunk, (s+1)*chunk) of the
- * concatenated cache. Each slot is cut at sequence boundaries into items;
- * an item covering a whole sequence writes its output directly, any other
- * item writes a partial (acc, LSE) merged afterwards by the reduce kernel.
+ * c0 = max(MLA_PLAN_MIN_CHUNK, round_up(ceil(T/G), MLA_PLAN_CHUNK_ALIGN)) is
+ * the equal-token slot. When c0 > MLA_PLAN_ITEM_COST, a sequence of length
+ * 0 < n < c0 is short: it shares its slot with others and each of its items
+ * adds fixed work. The sequences are laid end to end on a weighted line, a
+ * short one taking MLA_PLAN_ITEM_COST units and then its n tokens, a long
+ * one its tokens only (so with no short sequence the line is the token
+ * stream); Wt is the line's length, chunk = max(MLA_PLAN_MIN_CHUNK,
+ * round_up(ceil(Wt/G), MLA_PLAN_CHUNK_ALIGN)), and slot s owns the units
+ * [s*chunk, (s+1)*chunk). Each slot's tokens are cut at sequence boundaries
+ * into items; an item covering a whole sequence writes its output directly,
+ * any other item writes a partial (acc, LSE) merged afterwards by the
+ * reduce kernel.
  *
  * Errors: MLA_ERR_INVALID for batch < 0, a null indptr (batch > 0),
  * indptr[0] < 0, decreasing offsets, more than 2^31-1 tokens or a null or

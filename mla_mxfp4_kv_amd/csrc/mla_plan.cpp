@@ -7,7 +7,9 @@
 // chunks. Here the concatenated token stream is cut into `num_slots` equal
 // contiguous slots, one per workgroup of the device, so every workgroup
 // streams the same number of KV bytes whatever the length mix; slots are then
-// cut at sequence boundaries into items.
+// cut at sequence boundaries into items. When workgroups have more than an
+// item's fixed work to stream, short sequences are charged that work, so a
+// slot that holds several of them gets fewer tokens.
 #include <algorithm>
 #include <climits>
 #include <cstring>
@@ -67,13 +69,30 @@ int build_plan(const int32_t* ind, int32_t batch, int32_t num_cus, PlanResult* o
   const int64_t total = end - base;
   const int64_t g = (int64_t)num_cus * MLA_PLAN_WG_PER_CU;
 
+  // Item charges: when an equal-token slot (c0) is longer than the fixed
+  // work of an item, sequences shorter than c0 share slots, and each of
+  // their items costs MLA_PLAN_ITEM_COST tokens' worth besides its tokens.
+  // Sequences are laid end to end on a weighted line, a short one taking its
+  // charge and then its tokens, and the line is cut into equal slots.
+  std::vector<int64_t> start(batch + 1, 0), tok0(batch, 0);
+  bool charge = false;
+  if (total > 0) {
+    const int64_t c0 = std::max<int64_t>(MLA_PLAN_MIN_CHUNK, round_up(ceil_div(total, g), MLA_PLAN_CHUNK_ALIGN));
+    charge = c0 > MLA_PLAN_ITEM_COST;
+    int64_t pos = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t len = (int64_t)ind[b + 1] - ind[b];
+      start[b] = pos;
+      tok0[b] = pos + (charge && len > 0 && len < c0 ? MLA_PLAN_ITEM_COST : 0);
+      pos = tok0[b] + len;
+    }
+    start[batch] = pos;
+  }
+  const int64_t wt = start[batch];
   int64_t chunk = 0, num_slots = 0;
   if (total > 0) {
-    chunk = std::max<int64_t>(MLA_PLAN_MIN_CHUNK, round_up(ceil_div(total, g), MLA_PLAN_CHUNK_ALIGN));
-    // the chunk is an int32 plan word: one past INT32_MAX covers the whole
-    // stream anyway, and is stored as its length (the same single slot)
-    if (chunk > INT32_MAX) chunk = total;
-    num_slots = ceil_div(total, chunk);
+    chunk = std::max<int64_t>(MLA_PLAN_MIN_CHUNK, round_up(ceil_div(wt, g), MLA_PLAN_CHUNK_ALIGN));
+    num_slots = ceil_div(wt, chunk);
   }
 
   // Items, walking slots in order; a sequence that spans slots gets one
@@ -86,13 +105,14 @@ int build_plan(const int32_t* ind, int32_t batch, int32_t num_cus, PlanResult* o
   int32_t num_partials = 0;
   int32_t seq = 0;
   for (int64_t s = 0; s < num_slots; ++s) {
-    const int64_t lo = base + s * chunk;
-    const int64_t hi = std::min(base + (s + 1) * chunk, end);
-    while (seq < batch && ind[seq + 1] <= lo) ++seq;
-    for (int32_t b = seq; b < batch && ind[b] < hi; ++b) {
+    const int64_t lo = s * chunk, hi = (s + 1) * chunk;
+    while (seq < batch && start[seq + 1] <= lo) ++seq;
+    for (int32_t b = seq; b < batch && start[b] < hi; ++b) {
+      // the part of sequence b's tokens inside [lo, hi) on the line
+      const int64_t u0 = std::max(lo, tok0[b]), u1 = std::min(hi, start[b + 1]);
+      if (u1 <= u0) continue;
       const int64_t sl = ind[b], sh = ind[b + 1];
-      if (sh <= sl) continue;
-      const int64_t il = std::max(lo, sl), ih = std::min(hi, sh);
+      const int64_t il = sl + (u0 - tok0[b]), ih = sl + (u1 - tok0[b]);
       int32_t dest = -1;
       if (!(il == sl && ih == sh)) {
         dest = num_partials++;
@@ -129,7 +149,7 @@ int build_plan(const int32_t* ind, int32_t batch, int32_t num_cus, PlanResult* o
   w[kPwBase] = (int32_t)base;
   w[kPwTotal] = (int32_t)total;
   w[kPwNumCus] = num_cus;
-  w[kPwChunk] = (int32_t)chunk;
+  w[kPwChunk] = (int32_t)std::min<int64_t>(chunk, INT32_MAX);   // a record of the rule's value
   w[kPwNumSlots] = (int32_t)num_slots;
   w[kPwNumItems] = (int32_t)n_items;
   w[kPwNumPartials] = num_partials;

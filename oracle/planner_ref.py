@@ -11,18 +11,34 @@ metadata builder; "kernelbot-amd-mixed-mla-676098", split heuristic aiming at
 about four workgroups per compute unit). The pages split each sequence into
 fixed 128-token chunks; the rule here instead cuts the concatenated token
 stream into equal contiguous slots, one per workgroup of the device, so that
-every workgroup streams the same number of KV bytes whatever the length mix.
+every workgroup streams about the same number of KV bytes whatever the
+length mix, with the fixed work of each item counted in where short
+sequences share slots.
 
 The rule (constants in ``PlanConsts``):
 
 * ``T = kv_indptr[B] - kv_indptr[0]``, ``G = num_cus * WG_PER_CU``.
-* ``chunk = max(MIN_CHUNK, round_up(ceil(T / G), CHUNK_ALIGN))``, or T when
-  that exceeds 2^31 - 1 (the chunk is an int32 plan word; either value
-  gives the same single slot);
-  ``num_slots = ceil(T / chunk)`` (0 when T is 0).
-* Slot s owns tokens ``[base + s*chunk, min(base + (s+1)*chunk, base + T))``.
-* The slot's range is cut at sequence boundaries, in ascending token order,
-  into items ``(b, kv_begin, kv_end, dest)``. Empty sequences give no item.
+* ``c0 = max(MIN_CHUNK, round_up(ceil(T / G), CHUNK_ALIGN))``: the slot
+  length that cuts the token stream alone into equal slots.
+* An item costs a fixed amount of work besides its tokens (its Q, its first
+  tile in flight, the merge of the workgroup's partial states, its stores),
+  about ITEM_COST tokens' worth. When ``c0 > ITEM_COST`` (every workgroup
+  has more than that to stream), a sequence with ``0 < len < c0`` is
+  *short*: it shares its slot with others, and each such item adds that
+  cost. Sequences are laid end to end on a weighted line: sequence b takes
+  ``ITEM_COST * short_b + len_b`` units starting at ``W_b`` (``W_0 = 0``),
+  the charge first and then its tokens (token ``kv_indptr[b] + j`` at
+  ``W_b + ITEM_COST * short_b + j``); ``Wt = W_B``. With no short sequence
+  the line is the token stream itself.
+* ``chunk = max(MIN_CHUNK, round_up(ceil(Wt / G), CHUNK_ALIGN))`` (at least
+  c0, so longer than ITEM_COST whenever a charge exists: no slot lies
+  wholly inside one, and every slot owns an item); ``num_slots = ceil(Wt /
+  chunk)`` (0 when T is 0). The chunk word stores ``min(chunk, 2^31 - 1)``
+  (it records the rule's value; nothing reads it back).
+* Slot s owns the units ``[s*chunk, (s+1)*chunk)``; its items are the
+  sequences whose tokens meet that range, each cut to it, in ascending b,
+  as token ranges ``(b, kv_begin, kv_end, dest)``. Empty sequences give no
+  item.
 * ``dest = -1`` when the item is the whole sequence (its output is written
   directly); otherwise ``dest`` is the next partial index, so the partials of
   one sequence are consecutive.
@@ -49,6 +65,7 @@ class PlanConsts:
     WG_PER_CU = 1
     CHUNK_ALIGN = 128
     MIN_CHUNK = 256
+    ITEM_COST = 512             # fixed work of one item, in tokens
     NUM_HEADS = 16
     V_DIM = 512
     ALIGN_BYTES = 256
@@ -96,39 +113,48 @@ def build_plan(kv_indptr, batch: int, num_cus: int) -> PlanRef:
         raise ValueError("token count must stay below 2^31")
 
     g = num_cus * c.WG_PER_CU
-    if total == 0:
-        chunk, num_slots = 0, 0
-    else:
-        chunk = max(c.MIN_CHUNK, _round_up(_cdiv(total, g), c.CHUNK_ALIGN))
-        if chunk > 2 ** 31 - 1:   # the chunk word is int32; the one slot it defines covers T
-            chunk = total
-        num_slots = _cdiv(total, chunk)
+    lens = [ind[i + 1] - ind[i] for i in range(batch)]
+    short = [0] * batch
+    if total:
+        c0 = max(c.MIN_CHUNK, _round_up(_cdiv(total, g), c.CHUNK_ALIGN))
+        if c0 > c.ITEM_COST:
+            short = [1 if 0 < n < c0 else 0 for n in lens]
+    # the weighted line: start of each sequence and start of its tokens
+    starts, tok0 = [], []
+    pos = 0
+    for i in range(batch):
+        starts.append(pos)
+        tok0.append(pos + c.ITEM_COST * short[i])
+        pos = tok0[-1] + lens[i]
+    starts.append(pos)
+    wt = pos
+    chunk, num_slots = 0, 0
+    if total:
+        chunk = max(c.MIN_CHUNK, _round_up(_cdiv(wt, g), c.CHUNK_ALIGN))
+        num_slots = _cdiv(wt, chunk)
 
-    plan = PlanRef(batch=batch, base=base, total=total, num_cus=num_cus, chunk=chunk)
+    plan = PlanRef(batch=batch, base=base, total=total, num_cus=num_cus,
+                   chunk=min(chunk, 2 ** 31 - 1))
     plan.slot_indptr.append(0)
     pieces = {}                      # b -> number of items
     first_partial = {}
-    b = 0
     for s in range(num_slots):
-        lo = base + s * chunk
-        hi = min(base + (s + 1) * chunk, end)
-        # first sequence whose range reaches past lo
-        while b < batch and ind[b + 1] <= lo:
-            b += 1
-        bb = b
-        while bb < batch and ind[bb] < hi:
-            seq_lo, seq_hi = ind[bb], ind[bb + 1]
-            if seq_hi > seq_lo:
-                it_lo, it_hi = max(lo, seq_lo), min(hi, seq_hi)
-                if it_lo == seq_lo and it_hi == seq_hi:
-                    dest = -1
-                else:
-                    dest = plan.num_partials
-                    plan.num_partials += 1
-                    first_partial.setdefault(bb, dest)
-                plan.items.append((bb, it_lo, it_hi, dest))
-                pieces[bb] = pieces.get(bb, 0) + 1
-            bb += 1
+        lo, hi = s * chunk, (s + 1) * chunk
+        for bb in range(batch):
+            # the part of sequence bb's tokens inside [lo, hi), on the line
+            u0, u1 = max(lo, tok0[bb]), min(hi, starts[bb + 1])
+            if u1 <= u0:
+                continue
+            it_lo = ind[bb] + (u0 - tok0[bb])
+            it_hi = ind[bb] + (u1 - tok0[bb])
+            if it_lo == ind[bb] and it_hi == ind[bb + 1]:
+                dest = -1
+            else:
+                dest = plan.num_partials
+                plan.num_partials += 1
+                first_partial.setdefault(bb, dest)
+            plan.items.append((bb, it_lo, it_hi, dest))
+            pieces[bb] = pieces.get(bb, 0) + 1
         plan.slot_indptr.append(len(plan.items))
 
     for bi in range(batch):
@@ -210,6 +236,8 @@ def workspace_bound_ref(batch: int, total: int, num_cus: int) -> int:
     if total <= 0:
         slots = 0
     else:
+        # short sequences exist only when a slot is longer than ITEM_COST,
+        # so the charges never shorten a slot below that (nor MIN_CHUNK)
         slots = min(g, _cdiv(total, c.MIN_CHUNK))
     items = slots + batch
     partials = 2 * slots

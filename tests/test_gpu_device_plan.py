@@ -63,6 +63,12 @@ PLAN_CASES = [
     ([256] * 10, 0, 10),
     ([255, 257, 1, 511, 513], 5, 7),
     ([2 ** 30, 2 ** 31 - 1 - 2 ** 30], 0, 1),     # the int32 token limit on one CU
+    # item charges: short sequences on a weighted line, across the
+    # 1024-sequence blocks of the planner's scans
+    ([5, 0, 300, 17] * 400, 3, 7),
+    ([3000, 200, 100, 700], 0, 2),
+    (synth.seq_lengths(synth.WORKLOADS["b128_ragged"]), 0, 256),
+    ([40000, 1, 2, 3] + [6000] * 60 + [5] * 30, 11, 256),
 ]
 
 

@@ -26,6 +26,30 @@ def test_hand_worked_plan_two_cus():
     assert need == 512 + 2 * 16 * 512 * 4
 
 
+def test_hand_worked_plan_with_item_charges():
+    # lens [3000, 200, 100, 700] on 2 CUs: T = 4000, ceil(4000/2) = 2000 ->
+    # c0 = 2048 > ITEM_COST = 512, so the sequences shorter than 2048 (b = 1,
+    # 2, 3) are short and each carries 512 units ahead of its tokens.
+    # Line: seq 0 tokens [0,3000); seq 1 charge [3000,3512), tokens
+    # [3512,3712); seq 2 charge [3712,4224), tokens [4224,4324); seq 3 charge
+    # [4324,4836), tokens [4836,5536). Wt = 5536 -> ceil(5536/2) = 2768 ->
+    # chunk 2816, 2 slots: [0,2816) and [2816,5632).
+    # Slot 0: seq 0 tokens [0,2816) -> partial 0.
+    # Slot 1: seq 0 [2816,3000) -> partial 1; seqs 1, 2, 3 whole.
+    # (The equal-token cut would give slot 1 the 952 tokens left of seq 0
+    # plus all three short sequences: four items against one.)
+    words, need = plan_words_ref([0, 3000, 3200, 3300, 4000], 4, 2)
+    hdr = [PlanConsts.MAGIC, 1, 4, 0, 4000, 2, 2816, 2, 5, 2, 1, 16, 20, 40]
+    assert words[:14] == hdr
+    assert words[16:19] == [0, 1, 5]
+    assert words[20:40] == [0, 0, 2816, 0, 0, 2816, 3000, 1, 1, 3000, 3200, -1,
+                            2, 3200, 3300, -1, 3, 3300, 4000, -1]
+    assert words[40:44] == [0, 0, 2, 0]
+    assert len(words) == 44
+    assert words[14] == 256 and words[15] == 512
+    assert need == 512 + 2 * 16 * 512 * 4
+
+
 def test_headline_shape_is_one_sequence_per_slot():
     ind = [8192 * i for i in range(257)]
     d = decode_plan_words(plan_words_ref(ind, 256, 256)[0])
@@ -69,27 +93,40 @@ def _check_invariants(ind, num_cus):
     total = end - base
     chunk = d["chunk"]
     assert need <= workspace_bound_ref(b_n, total, num_cus)
+    # which sequences carry the item charge (only when an equal-token slot is
+    # longer than the charge)
+    g = num_cus * PlanConsts.WG_PER_CU
+    c0 = max(PlanConsts.MIN_CHUNK, -(-(-(-total // g)) // PlanConsts.CHUNK_ALIGN) * PlanConsts.CHUNK_ALIGN)
+    lens = [ind[b + 1] - ind[b] for b in range(b_n)]
+    charged = [total > 0 and c0 > PlanConsts.ITEM_COST and 0 < n < c0 for n in lens]
     if total:
-        assert chunk >= PlanConsts.MIN_CHUNK and chunk % PlanConsts.CHUNK_ALIGN == 0
-        assert d["num_slots"] <= num_cus * PlanConsts.WG_PER_CU
-        assert (d["num_slots"] - 1) * chunk < total <= d["num_slots"] * chunk
-    covered = []
+        assert chunk >= max(PlanConsts.MIN_CHUNK, c0 if any(charged) else 0)
+        assert chunk % PlanConsts.CHUNK_ALIGN == 0
+        assert d["num_slots"] <= g
+    flat = []
     pieces = {}
     for s in range(d["num_slots"]):
-        lo, hi = base + s * chunk, min(base + (s + 1) * chunk, end)
         its = d["items"][d["slot_indptr"][s]:d["slot_indptr"][s + 1]]
         assert its, "every slot owns at least one item"
-        assert its[0][1] == lo and its[-1][2] == hi
         for a, c in zip(its, its[1:]):
             assert a[2] == c[1] and a[0] < c[0]
+        # a slot holds chunk units of the weighted line: its tokens plus the
+        # charges of the short sequences that start in it, give or take less
+        # than one charge cut by each edge
+        load = sum(ke - kb + PlanConsts.ITEM_COST * (charged[b] and kb == ind[b]) for (b, kb, ke, _) in its)
+        assert load < chunk + PlanConsts.ITEM_COST
+        if s < d["num_slots"] - 1:
+            assert load > chunk - PlanConsts.ITEM_COST
+            if not any(charged):
+                assert load == chunk
         for (b, kb, ke, dest) in its:
             assert ind[b] <= kb < ke <= ind[b + 1]
             assert (dest == -1) == (kb == ind[b] and ke == ind[b + 1])
-            covered.append((kb, ke))
+            flat.append((kb, ke))
             pieces.setdefault(b, []).append(dest)
-    covered.sort()
+    # slots in order cover the token stream in order, without gaps
     pos = base
-    for kb, ke in covered:
+    for kb, ke in flat:
         assert kb == pos
         pos = ke
     assert pos == end
