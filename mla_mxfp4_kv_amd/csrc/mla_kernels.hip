@@ -96,7 +96,6 @@ constexpr float kMInit = -1.0e30f;              // running max before the first 
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 static_assert(kTile * kRowBytes % 1024 == 0, "a tile's rows are whole 1 KB DMA instructions");
-static_assert(kRowDma + 1 < 16, "a tile's loads fit the low vmcnt field");
 
 // LDS layout by cache addressing. kGather (rows listed per token in
 // kv_indices) keeps each tile row's scale bytes in a 32-byte slot of its own
@@ -734,6 +733,12 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
 // (contiguous rows only): sequence b starts at row kv_start[b], so that
 // several entries can share rows. Each mode is its own instantiation; the
 // plain contiguous kernel carries none of the others' code.
+// One plan item: sequence, token range, partial index (-1: direct output).
+struct __attribute__((aligned(16))) ItemWords {
+  int32_t b, kb, ke, dest;
+};
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
+
 template <bool kGather, bool kPages, bool kStarts = false>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -768,10 +773,19 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int off_items = plan[kPwOffItems];
   int i_begin = slot_indptr[first_slot];
   int i_end = slot_indptr[first_slot + 1];
+  // The first slot's first item, read in the same batch from where it sits
+  // when the items start right after slot_indptr of a launch-sized plan and
+  // every slot before this one holds one item (item index = slot index).
+  // It is used only when the header and slot_indptr confirm both, else the
+  // item is loaded after them. The words read lie inside the plan in every
+  // case: a plan has at least the launched number of slots, its items start
+  // at or after this offset, and it has at least one item per slot.
+  const int spec_off = (MLA_PLAN_HEADER_WORDS + (int)gridDim.x + 1 + 3) & ~3;
+  const ItemWords spec = *(const ItemWords*)(plan + spec_off + 4 * first_slot);
   // (the compiler would otherwise load each only where it is first used,
   // one latency after another; the kernel arguments are fetched here too)
-  asm volatile("" ::"s"(num_slots), "s"(off_items), "s"(i_begin), "s"(i_end), "s"(q), "s"(kv), "s"(sc),
-               "s"(kv_indptr), "s"(out));
+  asm volatile("" ::"s"(num_slots), "s"(off_items), "s"(i_begin), "s"(i_end), "s"(spec.b), "s"(spec.kb),
+               "s"(spec.ke), "s"(spec.dest), "s"(q), "s"(kv), "s"(sc), "s"(kv_indptr), "s"(out));
   // Only words written by a planner are followed: a workspace whose header
   // is not a plan of this version (never planned, overwritten, or an
   // empty device plan) leaves the output untouched.
@@ -782,6 +796,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   csc = fabsf(csc);
 
   const int32_t* items = plan + off_items;
+  // kv_indptr is not written while the kernel runs: read it through the
+  // constant address space, so that its words come by scalar loads
+  const ConstI32* kv_indptr_s = (const ConstI32*)kv_indptr;
   uint8_t* ring = lds + pair * L::kPair;
   TileHandoff* hand = (TileHandoff*)(lds + L::kXchg) + pair * 64 + lane;  // + parity * kPairs * 64
   uint8_t* fmt_pair = lds + L::kFmt + pair * kFmtTile;  // + parity * kPairs * kFmtTile
@@ -795,32 +812,33 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       i_end = slot_indptr[slot + 1];
     }
     for (int it = i_begin; it < i_end; ++it) {
-      const int b = items[4 * it + 0];
-      const int seq_lo = kv_indptr[b];
-      const int seq_hi = kv_indptr[b + 1];
-      const int kb = max(items[4 * it + 1], seq_lo);
-      const int ke = min(items[4 * it + 2], seq_hi);
-      const int dest = items[4 * it + 3];
+      const ItemWords iw = slot == first_slot && it == first_slot && off_items == spec_off
+                               ? spec : *(const ItemWords*)(items + 4 * it);
+      const int b = iw.b;
+      const int dest = iw.dest;
       // first entry of the sequence in kv_indices: its page list, or its rows
       const int ibase = kPages ? page_indptr[b] : 0;   // the sequence's first page entry
-      // contiguous rows: with kv_start the sequence's tokens are the rows from
-      // kv_start[b] on (several sequences may share them); the tile code
-      // keeps kv_indptr positions and reads through shifted bases
-      const uint8_t* kv_b = kv;
-      const uint8_t* sc_b = sc;
-      if (kStarts) {
-        const ptrdiff_t shift = (ptrdiff_t)kv_start[b] - seq_lo;
-        kv_b += shift * kRowBytes;
-        sc_b += shift * kBlocks;
-      }
-
-      // counts from differences, so that offsets near 2^31 - 1 cannot wrap;
-      // a tile start is only formed for tiles inside the item (below ke)
-      const int len = ke - kb;
-      const int rounds = len > 0 ? (len - 1) / kTileStride + 1 : 0;
-      const int rel_first = kTile * pair;
-      const int ntiles = rel_first < len ? (len - rel_first - 1) / kTileStride + 1 : 0;
-      const int t_first = ntiles > 0 ? kb + rel_first : kb;
+      // The item's rows, clamped to the sequence (a plan made for other
+      // offsets reads nothing outside it). Each role takes them on its own
+      // path, the scorer after it has requested q (scalar loads here; the q
+      // loads are vector loads), so that q flies while they are waited for.
+      struct Range {
+        int seq_lo, kb, ke, rounds, ntiles, t_first;
+      };
+      auto item_range = [&]() {
+        Range r;
+        r.seq_lo = kv_indptr_s[b];
+        r.kb = max(iw.kb, r.seq_lo);
+        r.ke = min(iw.ke, kv_indptr_s[b + 1]);
+        // counts from differences, so that offsets near 2^31 - 1 cannot
+        // wrap; a tile start is only formed for tiles inside the item
+        const int len = r.ke - r.kb;
+        r.rounds = len > 0 ? (len - 1) / kTileStride + 1 : 0;
+        const int rel_first = kTile * pair;
+        r.ntiles = rel_first < len ? (len - rel_first - 1) / kTileStride + 1 : 0;
+        r.t_first = r.ntiles > 0 ? r.kb + rel_first : r.kb;
+        return r;
+      };
 
       // The pair splits a tile's work by role, each wave on its own loop
       // (both pass the same workgroup barriers, one per round):
@@ -837,8 +855,25 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
         st.m = kMInit;
         const QChunk qc = load_q_chunk(q + ((size_t)b * kHeads + col) * kQkDim, pair, grp);
+        const Range rg = item_range();
+        const int seq_lo = rg.seq_lo, ke = rg.ke, rounds = rg.rounds, ntiles = rg.ntiles, t_first = rg.t_first;
+        // contiguous rows: with kv_start the sequence's tokens are the rows
+        // from kv_start[b] on (several sequences may share them); the tile
+        // code keeps kv_indptr positions and reads through shifted bases
+        const uint8_t* kv_b = kv;
+        const uint8_t* sc_b = sc;
+        if (kStarts) {
+          const ptrdiff_t shift = (ptrdiff_t)kv_start[b] - seq_lo;
+          kv_b += shift * kRowBytes;
+          sc_b += shift * kBlocks;
+        }
         PageRows pages = {0u, 0u};   // page tables: the entries of the next tile to stage
         __syncthreads();  // LDS of the previous item's merge is free again
+        // Contiguous rows: q's loads went out before the bounds were waited
+        // for and have landed by now. Taking them here, before tile 0 is
+        // requested, lets the split below run while the tile flies (a wait
+        // for q after the tile's loads would also wait for the tile).
+        if constexpr (!kGather) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         if (ntiles > 0) {
           if constexpr (kPages) {
             // rows of tile 0, then its staging; the pages of tile 1 fly
@@ -858,14 +893,6 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           } else {
             stage_dma(ring, kv_b, sc_b, t_first, ke - t_first, lane);
           }
-        }
-        // This wave's chunk of q is split while tile 0 is in flight: only the
-        // q loads, older than the tile's kRowDma + 1 loads, are waited for.
-        if constexpr (!kGather) {
-          if (ntiles > 0)
-            __builtin_amdgcn_s_waitcnt(0x0f70 | (kRowDma + 1));   // vmcnt(kRowDma + 1)
-          else
-            __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0)
         }
         {
           i32x8_t qhi, qlo;
@@ -922,6 +949,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           for (int r = 0; r < 4; ++r) stats[(2 * pair + 1) * kHeads + 4 * grp + r] = st.l[r];
         }
       } else {
+        const Range rg = item_range();
+        const int rounds = rg.rounds, ntiles = rg.ntiles;
         f32x4_t o[32];
 #pragma unroll
         for (int n = 0; n < 32; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
