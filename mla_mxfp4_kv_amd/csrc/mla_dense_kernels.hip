@@ -483,6 +483,12 @@ __device__ __forceinline__ void pv_bf16(const uint8_t* buf, const bf16x4_t& pa, 
   pv_bf16_group<3>(ta, pa, o);
 }
 
+// One plan item: sequence, token range, partial index (-1: direct output).
+struct __attribute__((aligned(16))) ItemWords {
+  int32_t b, kb, ke, dest;
+};
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
+
 template <bool kFp8, bool kGather>
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -500,12 +506,31 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
   const int grp = lane >> 4;
   // Header words in one batch (the compiler would fetch each only after the
   // previous check, a memory latency apiece).
+  // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
+  // (kv_start), consecutive slots -- the query groups of one sequence --
+  // go to workgroups of one XCD, so that its L2 serves the repeated reads.
+  const bool xcd_order = !kGather && kv_start != nullptr && (gridDim.x & 7) == 0;
+  const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                   : (int)blockIdx.x;
+  // The first slot's bounds (slot_indptr follows the header in both
+  // planners' layouts, with an entry for every launched workgroup) and its
+  // first item, from where it sits when the items follow slot_indptr of a
+  // launch-sized plan with one item per slot before it, come in the same
+  // batch; the item is used only if the header and slot_indptr confirm that
+  // layout (the words read are inside the plan whatever it holds: it has at
+  // least the launched number of slots, items from this offset on, and an
+  // item per slot).
+  const int32_t* slot_indptr = plan + MLA_PLAN_HEADER_WORDS;
   const int magic = plan[kPwMagic];
   const int version = plan[kPwVersion];
   const int num_slots = plan[kPwNumSlots];
-  const int off_slot = plan[kPwOffSlot];
   const int off_items = plan[kPwOffItems];
-  asm volatile("" ::"s"(num_slots), "s"(off_slot), "s"(off_items), "s"(q), "s"(kv), "s"(kv_indptr), "s"(out));
+  const int i_begin0 = slot_indptr[first_slot];
+  const int i_end0 = slot_indptr[first_slot + 1];
+  const int spec_off = (MLA_PLAN_HEADER_WORDS + (int)gridDim.x + 1 + 3) & ~3;
+  const ItemWords spec = *(const ItemWords*)(plan + spec_off + 4 * first_slot);
+  asm volatile("" ::"s"(num_slots), "s"(off_items), "s"(i_begin0), "s"(i_end0), "s"(spec.b), "s"(spec.kb),
+               "s"(spec.ke), "s"(spec.dest), "s"(q), "s"(kv), "s"(kv_indptr), "s"(out));
   // Only words written by a planner are followed: a workspace whose header
   // is not a plan of this version leaves the output untouched.
   if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
@@ -514,30 +539,35 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
   if constexpr (kFp8) vs = kv_scale[0];
   const float sc2 = csc * vs;
 
-  const int32_t* slot_indptr = plan + off_slot;
   const int32_t* items = plan + off_items;
+  // kv_indptr is not written while the kernel runs: scalar loads through
+  // the constant address space
+  const ConstI32* kv_indptr_s = (const ConstI32*)kv_indptr;
   uint8_t* ring = lds + wave * (2 * kTileBytes);   // this wave's two tile buffers
   // merge area, over the tile buffers once every wave is done: the O tiles
   // of all waves, then the (m, l) statistics
   f32x4_t* frag = (f32x4_t*)lds;
   float* stats = (float*)(lds + 2 * kHalfFrag);
 
-  // Workgroups are dealt to the 8 XCDs in turn. When entries share rows
-  // (kv_start), consecutive slots -- the query groups of one sequence --
-  // go to workgroups of one XCD, so that its L2 serves the repeated reads.
-  const bool xcd_order = !kGather && kv_start != nullptr && (gridDim.x & 7) == 0;
-  const int first_slot = xcd_order ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
-                                   : (int)blockIdx.x;
   for (int slot = first_slot; slot < num_slots; slot += gridDim.x) {
-    const int i_begin = slot_indptr[slot];
-    const int i_end = slot_indptr[slot + 1];
+    const int i_begin = slot == first_slot ? i_begin0 : slot_indptr[slot];
+    const int i_end = slot == first_slot ? i_end0 : slot_indptr[slot + 1];
     for (int it = i_begin; it < i_end; ++it) {
-      const int b = items[4 * it + 0];
-      const int kb = max(items[4 * it + 1], kv_indptr[b]);
-      const int ke = min(items[4 * it + 2], kv_indptr[b + 1]);
-      const int dest = items[4 * it + 3];
+      const ItemWords iw = slot == first_slot && it == first_slot && off_items == spec_off
+                               ? spec : *(const ItemWords*)(items + 4 * it);
+      const int b = iw.b;
+      const int dest = iw.dest;
+      // bf16: q is requested before the bounds below are waited for (scalar
+      // loads; the q loads are vector loads), so that it flies meanwhile
+      const uint16_t* qh = q + ((size_t)b * kHeads + col) * kQkDim;
+      QBf16 q16;
+      if constexpr (!kFp8) q16 = load_q_bf16(qh, grp);
+      // the item's rows, clamped to the sequence (a plan made for other
+      // offsets reads nothing outside it)
+      const int seq_lo = kv_indptr_s[b];
+      const int kb = max(iw.kb, seq_lo);
+      const int ke = min(iw.ke, kv_indptr_s[b + 1]);
       // first entry of the sequence in kv_indices: its page list, or its rows
-      const int seq_lo = kv_indptr[b];
       const int ibase = kGather && page_indptr != nullptr ? page_indptr[b] : seq_lo;
       // contiguous rows from kv_start[b] on, when given (shared by sequences)
       const uint8_t* kv_b = kv;
@@ -549,19 +579,10 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
       const int ntiles = rel_first < len ? (len - rel_first - 1) / C::kStride + 1 : 0;
       const int t_first = ntiles > 0 ? kb + rel_first : kb;
 
-      const uint16_t* qh = q + ((size_t)b * kHeads + col) * kQkDim;
+      // fp8: q is loaded and split chunk by chunk as it lands (measured
+      // faster than splitting it whole under tile 0's flight)
       QFp8 q8;
-      QBf16 q16;
-      if constexpr (kFp8) {
-        q8 = load_q_fp8(qh, grp);
-      } else {
-        q16 = load_q_bf16(qh, grp);
-        // take the q loads here, before the tile loop, so that no wait for
-        // them (which would also wait for the tile loads) lands in the loop
-#pragma unroll
-        for (int s = 0; s < 18; ++s) asm volatile("" : "+v"(q16.q[s]));
-      }
-
+      if constexpr (kFp8) q8 = load_q_fp8(qh, grp);
       float m = kMInit;    // running max of head col (base-2 scaled scores)
       float l = 0.f;       // this lane's share of head col's denominator
       f32x4_t o[kOFrags];
@@ -569,6 +590,10 @@ mla_decode_dense_kernel(const uint16_t* __restrict__ q, const uint8_t* __restric
       for (int n = 0; n < kOFrags; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
       __syncthreads();   // the previous item's merge has read the merge area
+      // q has landed by now. Taking it here, before tile 0 is requested,
+      // puts no wait for it in the loop (a wait for q after the tile's
+      // loads would also wait for the tile).
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
       // Score tile i (landed in `buf`) and accumulate it into O.
       auto compute = [&](const uint8_t* buf, int i) {
         const int t0 = t_first + i * C::kStride;

@@ -84,7 +84,6 @@ constexpr int kQStageSc = kQStage + 2 * 64 * 8;
 
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget of one gfx950 CU");
 static_assert(kLdsBuf % 64 == 0, "buffers stay 64-byte aligned");
-static_assert(kRowDma + 1 < 16, "a tile's loads fit the low vmcnt field");
 static_assert(kSteps == 6 && kQkDim == kSteps * 4 * kBlk, "six steps of four 24-element blocks");
 static_assert(kQStageSc <= kLdsMain - kLdsFmt, "the q stage fits the V-scale and hand-off areas");
 
@@ -557,6 +556,12 @@ __device__ __forceinline__ void pv_tile(const uint8_t* buf, const uint8_t* fmt, 
   pv_block<0>(tra, sca, v_cur, s_lo, s_hi, pa, o);
 }
 
+// One plan item: sequence, token range, partial index (-1: direct output).
+struct __attribute__((aligned(16))) ItemWords {
+  int32_t b, kb, ke, dest;
+};
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
+
 __global__ void __launch_bounds__(kThreads, 1)
 mla_decode_mxfp4_24_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                            const uint8_t* __restrict__ sc, const int32_t* __restrict__ kv_indptr,
@@ -579,14 +584,24 @@ mla_decode_mxfp4_24_kernel(const uint16_t* __restrict__ q, const uint8_t* __rest
   const int off_items = plan[kPwOffItems];
   int i_begin = slot_indptr[blockIdx.x];
   int i_end = slot_indptr[blockIdx.x + 1];
-  asm volatile("" ::"s"(num_slots), "s"(off_items), "s"(i_begin), "s"(i_end), "s"(q), "s"(kv), "s"(sc),
-               "s"(kv_indptr), "s"(out));
+  // the first slot's first item, from where it sits when the items follow
+  // slot_indptr of a launch-sized plan with one item per slot before it;
+  // used only if the header and slot_indptr confirm that (the words read
+  // are inside the plan whatever it holds: it has at least the launched
+  // number of slots, items from this offset on, and an item per slot)
+  const int spec_off = (MLA_PLAN_HEADER_WORDS + (int)gridDim.x + 1 + 3) & ~3;
+  const ItemWords spec = *(const ItemWords*)(plan + spec_off + 4 * (int)blockIdx.x);
+  asm volatile("" ::"s"(num_slots), "s"(off_items), "s"(i_begin), "s"(i_end), "s"(spec.b), "s"(spec.kb),
+               "s"(spec.ke), "s"(spec.dest), "s"(q), "s"(kv), "s"(sc), "s"(kv_indptr), "s"(out));
   // only words written by a planner are followed
   if (magic != MLA_PLAN_MAGIC || version != MLA_PLAN_VERSION) return;
   const uint32_t qsign = csc < 0.f ? 0x80008000u : 0u;
   csc = fabsf(csc);
 
   const int32_t* items = plan + off_items;
+  // kv_indptr is not written while the kernel runs: scalar loads through
+  // the constant address space
+  const ConstI32* kv_indptr_s = (const ConstI32*)kv_indptr;
   uint8_t* ring = lds + pair * kLdsPair;
   TileHandoff* hand = (TileHandoff*)(lds + kLdsXchg) + pair * 64 + lane;  // + parity * kPairs * 64
   uint8_t* fmt_pair = lds + kLdsFmt + pair * kFmtTile;                     // + parity * kPairs * kFmtTile
@@ -599,15 +614,27 @@ mla_decode_mxfp4_24_kernel(const uint16_t* __restrict__ q, const uint8_t* __rest
       i_end = slot_indptr[slot + 1];
     }
     for (int it = i_begin; it < i_end; ++it) {
-      const int b = items[4 * it + 0];
-      const int kb = max(items[4 * it + 1], kv_indptr[b]);
-      const int ke = min(items[4 * it + 2], kv_indptr[b + 1]);
-      const int dest = items[4 * it + 3];
-      const int len = ke - kb;
-      const int rounds = len > 0 ? (len - 1) / kTileStride + 1 : 0;
-      const int rel_first = kTile * pair;
-      const int ntiles = rel_first < len ? (len - rel_first - 1) / kTileStride + 1 : 0;
-      const int t_first = ntiles > 0 ? kb + rel_first : kb;
+      const ItemWords iw = slot == (int)blockIdx.x && it == (int)blockIdx.x && off_items == spec_off
+                               ? spec : *(const ItemWords*)(items + 4 * it);
+      const int b = iw.b;
+      const int dest = iw.dest;
+      // the item's rows clamped to the sequence; each role takes them on its
+      // own path, the scorer after it has requested q, so that q flies while
+      // these scalar loads are waited for
+      struct Range {
+        int ke, rounds, ntiles, t_first;
+      };
+      auto item_range = [&]() {
+        Range r;
+        const int kb = max(iw.kb, kv_indptr_s[b]);
+        r.ke = min(iw.ke, kv_indptr_s[b + 1]);
+        const int len = r.ke - kb;
+        r.rounds = len > 0 ? (len - 1) / kTileStride + 1 : 0;
+        const int rel_first = kTile * pair;
+        r.ntiles = rel_first < len ? (len - rel_first - 1) / kTileStride + 1 : 0;
+        r.t_first = r.ntiles > 0 ? kb + rel_first : kb;
+        return r;
+      };
 
       f32x4_t* frag = (f32x4_t*)lds;
       float* stats = (float*)(lds + kMergeFrag);
@@ -620,13 +647,14 @@ mla_decode_mxfp4_24_kernel(const uint16_t* __restrict__ q, const uint8_t* __rest
         const QChunk qa = load_q_chunk(qh, pair, grp);
         QChunk qb;
         if (pair < kSteps - 4) qb = load_q_chunk(qh, 4 + pair, grp);
+        const Range rg = item_range();
+        const int ke = rg.ke, rounds = rg.rounds, ntiles = rg.ntiles, t_first = rg.t_first;
         __syncthreads();  // LDS of the previous item's merge is free again
+        // q has landed by now; taking it before tile 0 is requested lets the
+        // split run while the tile flies (a wait for q after the tile's
+        // loads would also wait for the tile)
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         if (ntiles > 0) stage_dma(ring, kv, sc, t_first, ke - t_first, lane);
-        // only the q loads, older than the tile's kRowDma + 1 loads, are waited for
-        if (ntiles > 0)
-          __builtin_amdgcn_s_waitcnt(0x0f70 | (kRowDma + 1));   // vmcnt(kRowDma + 1)
-        else
-          __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0)
         {
           i32x8_t qhi, qlo;
           uint32_t qsh, qsl;
@@ -672,6 +700,8 @@ mla_decode_mxfp4_24_kernel(const uint16_t* __restrict__ q, const uint8_t* __rest
           for (int r = 0; r < 4; ++r) stats[(2 * pair + 1) * kHeads + 4 * grp + r] = st.l[r];
         }
       } else {
+        const Range rg = item_range();
+        const int rounds = rg.rounds, ntiles = rg.ntiles;
         f32x4_t o[32];
 #pragma unroll
         for (int n = 0; n < 32; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
