@@ -38,15 +38,15 @@ def _cases():
 
 
 @pytest.fixture(scope="module")
-def driver(tmp_path_factory):
+def harness(tmp_path_factory):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("g++ not available")
-    out = str(tmp_path_factory.mktemp("asan") / "plan_driver")
+    out = str(tmp_path_factory.mktemp("asan") / "plan_harness")
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc"),
-           os.path.join(ROOT, "tests", "native", "plan_driver.cpp"),
+           os.path.join(ROOT, "tests", "native", "plan_harness.cpp"),
            os.path.join(ROOT, "mla_mxfp4_kv_amd", "csrc", "mla_plan.cpp"), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -54,11 +54,11 @@ def driver(tmp_path_factory):
     return out
 
 
-def test_planner_under_sanitizers_matches_oracle(driver):
+def test_planner_under_sanitizers_matches_oracle(harness):
     cases = _cases()
     text = "".join(f"{cus} {len(ind) - 1} {' '.join(map(str, ind))}\n" for cus, ind in cases)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
-    res = subprocess.run([driver], input=text, capture_output=True, text=True, env=env, timeout=300)
+    res = subprocess.run([harness], input=text, capture_output=True, text=True, env=env, timeout=300)
     assert res.returncode == 0, res.stderr[-3000:]
     assert "runtime error" not in res.stderr and "AddressSanitizer" not in res.stderr, res.stderr[-3000:]
     lines = res.stdout.splitlines()
@@ -72,8 +72,8 @@ def test_planner_under_sanitizers_matches_oracle(driver):
         assert [int(x) for x in f[5:]] == words, (cus, ind[:5])
 
 
-def test_planner_under_sanitizers_refuses_bad_offsets(driver):
+def test_planner_under_sanitizers_refuses_bad_offsets(harness):
     text = "4 2 0 5 3\n4 1 -1 5\n0 1 0 5\n"
-    res = subprocess.run([driver], input=text, capture_output=True, text=True, timeout=60)
+    res = subprocess.run([harness], input=text, capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stderr[-3000:]
     assert res.stdout.split("\n")[:3] == ["error -1", "error -1", "error -1"]
