@@ -522,6 +522,19 @@ def test_split_invariance():
         assert np.linalg.norm(o - outs[0]) / np.linalg.norm(outs[0]) <= PAIRWISE
 
 
+@pytest.mark.parametrize("lens,num_cus", [([120000, 300, 40000, 5], 600), ([160000, 300, 60000, 5], 300)])
+def test_more_slots_than_workgroups(lens, num_cus):
+    """Plans for more slots than the device has CUs (418 and 289): the grid
+    stays at one workgroup per CU and each workgroup walks several slots
+    (the first slot's item read with the header does not apply to the later
+    ones). The 300-CU plan has item charges on (two short sequences)."""
+    _say(f"case more slots than workgroups lens={lens} num_cus={num_cus}")
+    q, packed, scales, indptr, _ = _small(lens, seed=31)
+    want = ref.mla_decode_ref(_qbits(q), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    got = _run(q, packed, scales, indptr.tolist(), num_cus)
+    _check(got, want, f"num_cus={num_cus}")
+
+
 def test_deterministic():
     _say("case determinism")
     q, packed, scales, indptr, _ = _small([4000, 123], seed=3)

@@ -126,6 +126,16 @@ def test_token_scaled_and_wide_query(fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+def test_more_slots_than_workgroups(fmt):
+    """A plan for 600 slots on a device with fewer CUs: each workgroup walks
+    several slots."""
+    _say(f"case {fmt} more slots than workgroups")
+    q, cache, scale, indptr, _ = _inputs(fmt, [120000, 300, 40000, 5], seed=31)
+    got = _run(fmt, q, cache, scale, indptr.tolist(), num_cus=600)
+    _check(got, _oracle(fmt, q, cache, scale, indptr.numpy()), f"{fmt} 600 slots")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_split_invariance(fmt):
     """The same inputs planned on 1, 7, 64 and all CUs (different splits and
     reduce merges) agree to the bf16 output rounding."""

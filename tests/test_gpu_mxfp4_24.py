@@ -92,6 +92,16 @@ def test_small_cases_match_oracle(lens, num_cus):
     _check(got, want, f"lens={lens}")
 
 
+def test_more_slots_than_workgroups():
+    """A plan for 600 slots on a device with fewer CUs: each workgroup walks
+    several slots."""
+    _say("case 24-scale more slots than workgroups")
+    q, packed, scales, indptr, _ = _inputs([120000, 300, 40000, 5], seed=31)
+    got = _run(q, packed, scales, indptr.tolist(), num_cus=600)
+    want = r24.mla_decode_ref_24(_qbits(q), packed.numpy(), scales.numpy(), indptr.numpy(), SM)
+    _check(got, want, "600 slots")
+
+
 def test_one_token_is_exact():
     """One token: p = 1, so the output is that token's V (bf16-exact)."""
     _say("case 24-scale one-token exactness")
