@@ -250,7 +250,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures the decode kernel on one GPU; runs over several GPUs are not "
-              "implemented (the decode would shard by sequence, see the design notes). Use --gpus 1.",
+              "implemented (the decode would shard by sequence: each GPU plans and decodes its own). Use --gpus 1.",
               file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
