@@ -19,7 +19,7 @@ def test_kv_bytes_per_format():
     assert synth.kv_bytes(1) == 288 + 18
     assert synth.kv_bytes(10, "fp8") == 5760
     assert synth.kv_bytes(10, "bf16") == 11520
-    # the headline cache sizes quoted in the benchmark and the design notes
+    # the cache sizes of 256 sequences of 8192 tokens
     assert synth.kv_bytes(256 * 8192) == 641728512
     assert synth.kv_bytes(256 * 8192, "fp8") == 1207959552
     assert synth.kv_bytes(256 * 8192, "bf16") == 2415919104
