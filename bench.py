@@ -217,7 +217,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="b256_kv8192", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--kv-format", default="mxfp4", choices=["mxfp4", "fp8", "bf16", "mxfp4_24"],
-                    help="cache format: the MXFP4 headline path (18 scales per token), the 24-scale MXFP4 "
+                    help="cache format: the MXFP4 path (18 scales per token), the 24-scale MXFP4 "
                          "layout, or the fp8 / bf16 sibling decodes")
     ap.add_argument("--gather", type=int, default=0, metavar="PAGE",
                     help="scatter the rows over the pool in pages of PAGE rows (seeded shuffle) and "

@@ -148,7 +148,7 @@ def test_gather_errors():
 
 
 def test_gather_workload_b256_page_shuffled():
-    """The headline workload with its rows scattered over the pool in 16-row
+    """B=256, kv=8192 with its rows scattered over the pool in 16-row
     pages (a paged cache), every sequence against the oracle."""
     w = synth.WORKLOADS["b256_kv8192"]
     _say("case gather b256_kv8192: generating")

@@ -163,7 +163,7 @@ def test_page_table_matches_oracle(fmt, lens, ps, num_cus):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
-def test_headline_workload_in_16_row_pages(fmt):
+def test_b256_kv8192_in_16_row_pages(fmt):
     """B=256, kv=8192 with every sequence in shuffled 16-row pages: bit
     identical to the row-list decode of the same rows, and every sequence
     against the oracle."""

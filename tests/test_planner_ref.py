@@ -50,7 +50,7 @@ def test_hand_worked_plan_with_item_charges():
     assert need == 512 + 2 * 16 * 512 * 4
 
 
-def test_headline_shape_is_one_sequence_per_slot():
+def test_b256_kv8192_is_one_sequence_per_slot():
     ind = [8192 * i for i in range(257)]
     d = decode_plan_words(plan_words_ref(ind, 256, 256)[0])
     assert d["chunk"] == 8192 and d["num_slots"] == 256
